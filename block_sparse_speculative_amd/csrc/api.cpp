@@ -1,0 +1,327 @@
+// C ABI of libsv: host-side validation, workspace carving, split choice and
+// dispatch to the HIP launchers. No device memory is allocated or freed here and
+// nothing synchronises; every entry point validates what the host can see before
+// it enqueues anything.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+#include "sv.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sv_status fail(sv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sv_status ok() {
+  g_last_error.clear();
+  return SV_OK;
+}
+
+sv_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxBlocksPerSeq = 16384;
+constexpr int kMaxDraft = 16;
+constexpr int kMaxRows = 128;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Validates the shape; `what` names the entry point for the message.
+sv_status check_shape(const sv_shape* s, const char* what) {
+  if (!s) return fail(SV_ERR_NULL_ARG, "%s: shape is NULL", what);
+  if (s->num_seqs < 0) return fail(SV_ERR_BAD_SHAPE, "%s: num_seqs < 0", what);
+  if (s->num_q_heads <= 0 || s->num_kv_heads <= 0)
+    return fail(SV_ERR_BAD_SHAPE, "%s: head counts must be positive", what);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(SV_ERR_BAD_SHAPE, "%s: num_q_heads (%d) not a multiple of num_kv_heads (%d)",
+                what, s->num_q_heads, s->num_kv_heads);
+  if (s->max_blocks_per_seq <= 0 || s->num_phys_blocks <= 0)
+    return fail(SV_ERR_BAD_SHAPE, "%s: max_blocks_per_seq and num_phys_blocks must be positive",
+                what);
+  if (s->num_draft <= 0) return fail(SV_ERR_BAD_SHAPE, "%s: num_draft must be positive", what);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(SV_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", what, s->head_dim);
+  if (s->block_size != 32 && s->block_size != 64 && s->block_size != 128)
+    return fail(SV_ERR_UNSUPPORTED, "%s: block_size %d not in {32, 64, 128}", what,
+                s->block_size);
+  if (s->num_draft > kMaxDraft)
+    return fail(SV_ERR_UNSUPPORTED, "%s: num_draft %d > %d", what, s->num_draft, kMaxDraft);
+  const int group = s->num_q_heads / s->num_kv_heads;
+  if (static_cast<int64_t>(s->num_draft) * group > kMaxRows)
+    return fail(SV_ERR_UNSUPPORTED, "%s: num_draft * group = %d > %d", what,
+                s->num_draft * group, kMaxRows);
+  if (s->dtype != SV_F32 && s->dtype != SV_BF16)
+    return fail(SV_ERR_UNSUPPORTED, "%s: dtype %d not supported", what, s->dtype);
+  if (s->max_blocks_per_seq > kMaxBlocksPerSeq)
+    return fail(SV_ERR_UNSUPPORTED, "%s: max_blocks_per_seq %d > %d", what,
+                s->max_blocks_per_seq, kMaxBlocksPerSeq);
+  return SV_OK;
+}
+
+sv_status check_budget(const sv_budget* b, const char* what) {
+  if (!b) return fail(SV_ERR_NULL_ARG, "%s: budget is NULL", what);
+  if (b->dense_ctx_tokens < 0 || b->min_blocks < 0 || b->frac_per_mille < 0 ||
+      b->frac_per_mille > 1000)
+    return fail(SV_ERR_BAD_SHAPE, "%s: budget fields out of range", what);
+  if ((b->keep_first != 0 && b->keep_first != 1) || (b->keep_last != 0 && b->keep_last != 1))
+    return fail(SV_ERR_BAD_SHAPE, "%s: keep_first / keep_last must be 0 or 1", what);
+  if (b->min_blocks < b->keep_first + b->keep_last)
+    return fail(SV_ERR_BAD_SHAPE, "%s: min_blocks %d smaller than the forced blocks", what,
+                b->min_blocks);
+  return SV_OK;
+}
+
+sv_status check_kmax(const sv_shape* s, int32_t k_max, const char* what) {
+  if (k_max <= 0 || k_max > s->max_blocks_per_seq)
+    return fail(SV_ERR_BAD_SHAPE, "%s: k_max %d not in [1, max_blocks_per_seq=%d]", what, k_max,
+                s->max_blocks_per_seq);
+  return SV_OK;
+}
+
+int resolve_splits(const sv_shape* s, int32_t k_max, int32_t num_splits) {
+  const int tt = sv::attn_tile_tokens(s->block_size);
+  const int64_t ctx_tiles = static_cast<int64_t>(k_max) * (s->block_size / tt);
+  int64_t want = num_splits;
+  if (want <= 0) {
+    const int64_t units = static_cast<int64_t>(s->num_seqs) * s->num_kv_heads;
+    const int64_t target_wgs = 256;
+    want = units > 0 ? (target_wgs + units - 1) / units : 1;
+  }
+  if (want > ctx_tiles) want = ctx_tiles;
+  if (want < 1) want = 1;
+  return static_cast<int>(want);
+}
+
+size_t select_ws_layout(const sv_shape* s, size_t* scores_off) {
+  const size_t units = static_cast<size_t>(s->num_seqs) * s->num_kv_heads;
+  const size_t tickets = align_up(units * sizeof(uint32_t));
+  *scores_off = tickets;
+  return tickets + align_up(units * s->max_blocks_per_seq * sizeof(float));
+}
+
+size_t attn_ws_layout(const sv_shape* s, int splits, size_t* ml_off) {
+  if (splits <= 1) {
+    *ml_off = 0;
+    return 0;
+  }
+  const size_t rows = static_cast<size_t>(s->num_draft) * (s->num_q_heads / s->num_kv_heads);
+  const size_t units = static_cast<size_t>(s->num_seqs) * s->num_kv_heads;
+  const size_t o = align_up(units * splits * rows * s->head_dim * sizeof(float));
+  *ml_off = o;
+  return o + align_up(units * splits * rows * 2 * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char* sv_status_str(int32_t status) {
+  switch (status) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_NULL_ARG: return "SV_ERR_NULL_ARG";
+    case SV_ERR_BAD_SHAPE: return "SV_ERR_BAD_SHAPE";
+    case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED";
+    case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE";
+    case SV_ERR_HIP: return "SV_ERR_HIP";
+    default: return "SV_ERR_UNKNOWN";
+  }
+}
+
+const char* sv_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sv_budget_blocks(const sv_budget* budget, int32_t ctx_len, int32_t block_size) {
+  if (!budget || ctx_len < 0 || block_size <= 0) return -1;
+  if (budget->dense_ctx_tokens < 0 || budget->min_blocks < 0 || budget->frac_per_mille < 0 ||
+      budget->frac_per_mille > 1000 ||
+      budget->min_blocks < (budget->keep_first != 0) + (budget->keep_last != 0))
+    return -1;
+  const int64_t nb = (static_cast<int64_t>(ctx_len) + block_size - 1) / block_size;
+  if (ctx_len <= budget->dense_ctx_tokens) return static_cast<int32_t>(nb);
+  int64_t k = (static_cast<int64_t>(budget->frac_per_mille) * nb + 999) / 1000;
+  if (k < budget->min_blocks) k = budget->min_blocks;
+  if (k > nb) k = nb;
+  return static_cast<int32_t>(k);
+}
+
+sv_status sv_block_repr(const sv_shape* shape, const void* k_new, const void* v_new,
+                        int32_t n_new_max, const int32_t* n_new, const int32_t* ctx_before,
+                        const int32_t* block_table, void* k_pool, void* v_pool, float* repr_pool,
+                        void* stream) {
+  const char* what = "sv_block_repr";
+  if (sv_status st = check_shape(shape, what)) return st;
+  if (n_new_max < 0) return fail(SV_ERR_BAD_SHAPE, "%s: n_new_max < 0", what);
+  if (n_new_max > 0 && shape->num_seqs > 0) {
+    if (!k_new || !v_new || !n_new || !ctx_before || !block_table || !k_pool || !v_pool ||
+        !repr_pool)
+      return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  }
+  if (n_new_max > static_cast<int64_t>(shape->max_blocks_per_seq) * shape->block_size)
+    return fail(SV_ERR_BAD_SHAPE, "%s: n_new_max exceeds the sequence capacity", what);
+  sv::ReprParams p{k_new, v_new, n_new, ctx_before, block_table, k_pool, v_pool, repr_pool,
+                   shape->num_seqs, shape->num_kv_heads, shape->head_dim, shape->block_size,
+                   shape->max_blocks_per_seq, shape->num_phys_blocks, n_new_max};
+  return from_hip(sv::launch_block_repr(p, shape->dtype == SV_BF16,
+                                        static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+size_t sv_select_workspace_bytes(const sv_shape* shape, int32_t k_max) {
+  (void)k_max;
+  if (check_shape(shape, "sv_select_workspace_bytes") != SV_OK) return 0;
+  size_t off;
+  return select_ws_layout(shape, &off);
+}
+
+sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const void* q,
+                           const float* repr_pool, const int32_t* block_table,
+                           const int32_t* ctx_lens, int32_t k_max, int32_t* idx, int32_t* cnt,
+                           float* scores, void* ws, size_t ws_bytes, void* stream) {
+  const char* what = "sv_select_blocks";
+  if (sv_status st = check_shape(shape, what)) return st;
+  if (sv_status st = check_budget(budget, what)) return st;
+  if (sv_status st = check_kmax(shape, k_max, what)) return st;
+  if (shape->num_seqs == 0) return ok();
+  if (!q || !repr_pool || !block_table || !ctx_lens || !idx || !cnt)
+    return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  size_t scores_off;
+  const size_t need = select_ws_layout(shape, &scores_off);
+  if (!ws || ws_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  char* w = static_cast<char*>(ws);
+  sv::SelectParams p{};
+  p.q = q;
+  p.repr_pool = repr_pool;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.idx = idx;
+  p.cnt = cnt;
+  p.scores = scores ? scores : reinterpret_cast<float*>(w + scores_off);
+  p.scores_requested = scores != nullptr;
+  p.tickets = reinterpret_cast<uint32_t*>(w);
+  p.B = shape->num_seqs;
+  p.Hq = shape->num_q_heads;
+  p.Hkv = shape->num_kv_heads;
+  p.G = shape->num_q_heads / shape->num_kv_heads;
+  p.D = shape->head_dim;
+  p.T = shape->num_draft;
+  p.bs = shape->block_size;
+  p.NB = shape->max_blocks_per_seq;
+  p.P = shape->num_phys_blocks;
+  p.k_max = k_max;
+  p.dense_ctx = budget->dense_ctx_tokens;
+  p.min_blocks = budget->min_blocks;
+  p.frac_per_mille = budget->frac_per_mille;
+  p.keep_first = budget->keep_first;
+  p.keep_last = budget->keep_last;
+  return from_hip(sv::launch_select(p, shape->dtype == SV_BF16, static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+int32_t sv_attn_num_splits(const sv_shape* shape, int32_t k_max, int32_t num_splits) {
+  if (check_shape(shape, "sv_attn_num_splits") != SV_OK) return 0;
+  if (check_kmax(shape, k_max, "sv_attn_num_splits") != SV_OK) return 0;
+  return resolve_splits(shape, k_max, num_splits);
+}
+
+size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num_splits) {
+  if (check_shape(shape, "sv_attn_workspace_bytes") != SV_OK) return 0;
+  if (check_kmax(shape, k_max, "sv_attn_workspace_bytes") != SV_OK) return 0;
+  size_t off;
+  return attn_ws_layout(shape, resolve_splits(shape, k_max, num_splits), &off);
+}
+
+sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,
+                                const void* v_draft, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* ctx_lens,
+                                const int32_t* idx, const int32_t* cnt, int32_t k_max,
+                                float scale, int32_t num_splits, void* out, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+  const char* what = "sv_sparse_verify_attn";
+  if (sv_status st = check_shape(shape, what)) return st;
+  if (sv_status st = check_kmax(shape, k_max, what)) return st;
+  if (num_splits < 0) return fail(SV_ERR_BAD_SHAPE, "%s: num_splits < 0", what);
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return fail(SV_ERR_BAD_SHAPE, "%s: scale must be finite", what);
+  if (shape->num_seqs == 0) return ok();
+  if (!q || !k_draft || !v_draft || !k_pool || !v_pool || !block_table || !ctx_lens || !idx ||
+      !cnt || !out)
+    return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  const int splits = resolve_splits(shape, k_max, num_splits);
+  size_t ml_off;
+  const size_t need = attn_ws_layout(shape, splits, &ml_off);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  char* w = static_cast<char*>(ws);
+  sv::AttnParams p{};
+  p.q = q;
+  p.k_draft = k_draft;
+  p.v_draft = v_draft;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.idx = idx;
+  p.cnt = cnt;
+  p.out = out;
+  p.lse = lse;
+  p.part_o = need ? reinterpret_cast<float*>(w) : nullptr;
+  p.part_ml = need ? reinterpret_cast<float*>(w + ml_off) : nullptr;
+  p.B = shape->num_seqs;
+  p.Hq = shape->num_q_heads;
+  p.Hkv = shape->num_kv_heads;
+  p.G = shape->num_q_heads / shape->num_kv_heads;
+  p.D = shape->head_dim;
+  p.T = shape->num_draft;
+  p.bs = shape->block_size;
+  p.NB = shape->max_blocks_per_seq;
+  p.P = shape->num_phys_blocks;
+  p.k_max = k_max;
+  p.S = splits;
+  p.R = shape->num_draft * p.G;
+  p.scale_log2 = scale * 1.44269504088896340736f;
+  return from_hip(sv::launch_attn(p, shape->dtype == SV_BF16, static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+sv_status sv_reuse_indices(const sv_shape* shape, int32_t k_max, const int32_t* prev_idx,
+                           const int32_t* prev_cnt, int32_t* idx, int32_t* cnt, void* stream) {
+  const char* what = "sv_reuse_indices";
+  if (sv_status st = check_shape(shape, what)) return st;
+  if (sv_status st = check_kmax(shape, k_max, what)) return st;
+  if (shape->num_seqs == 0) return ok();
+  if (!prev_idx || !prev_cnt || !idx || !cnt)
+    return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  const int64_t units = static_cast<int64_t>(shape->num_seqs) * shape->num_kv_heads;
+  const int64_t n_idx = units * k_max;
+  auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + nb && y < x + na;
+  };
+  if (overlap(prev_idx, n_idx * 4, idx, n_idx * 4) || overlap(prev_cnt, units * 4, cnt, units * 4))
+    return fail(SV_ERR_BAD_SHAPE, "%s: source and destination overlap", what);
+  sv::ReuseParams p{prev_idx, prev_cnt, idx, cnt, n_idx, units};
+  return from_hip(sv::launch_reuse(p, static_cast<hipStream_t>(stream)), what);
+}
+
+}  // extern "C"

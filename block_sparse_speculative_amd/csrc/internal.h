@@ -1,0 +1,84 @@
+// Internal declarations shared by the libsv translation units (host launchers and
+// device helpers). Not part of the public ABI; see include/sv.h for that.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+// ---------------------------------------------------------------- launch parameters
+
+struct ReprParams {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* n_new;
+  const int32_t* ctx_before;
+  const int32_t* block_table;
+  void* k_pool;
+  void* v_pool;
+  float* repr_pool;
+  int32_t B, Hkv, D, bs, NB, P, n_new_max;
+};
+
+struct SelectParams {
+  const void* q;
+  const float* repr_pool;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  int32_t* idx;
+  int32_t* cnt;
+  float* scores;        // [B, Hkv, NB] (user buffer or workspace)
+  uint32_t* tickets;    // [B * Hkv] arrival counters, zero between calls
+  int32_t scores_requested;   // nonzero: write scores even where every block is kept
+  int32_t B, Hq, Hkv, G, D, T, bs, NB, P, k_max;
+  int32_t dense_ctx, min_blocks, frac_per_mille, keep_first, keep_last;
+};
+
+struct AttnParams {
+  const void* q;
+  const void* k_draft;
+  const void* v_draft;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const int32_t* idx;
+  const int32_t* cnt;
+  void* out;
+  float* lse;
+  float* part_o;        // [units, S, R, D] unnormalised partial outputs
+  float* part_ml;       // [units, S, R, 2]  (running max in log2 units, denominator)
+  int32_t B, Hq, Hkv, G, D, T, bs, NB, P, k_max, S, R;
+  float scale_log2;     // softmax scale * log2(e)
+};
+
+struct ReuseParams {
+  const int32_t* prev_idx;
+  const int32_t* prev_cnt;
+  int32_t* idx;
+  int32_t* cnt;
+  int64_t n_idx;
+  int64_t n_cnt;
+};
+
+// ---------------------------------------------------------------- host launchers
+// Each returns hipSuccess or the launch error; shapes are validated by the caller.
+
+hipError_t launch_block_repr(const ReprParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_select(const SelectParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_reuse(const ReuseParams& p, hipStream_t stream);
+
+// Tokens per attention tile for a block size (a tile never spans two blocks).
+inline int attn_tile_tokens(int block_size) { return block_size < 64 ? block_size : 64; }
+
+// Padded row count of the (draft token x GQA head) tile.
+inline int attn_padded_rows(int rows) {
+  return rows <= 16 ? 16 : rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
+}
+
+constexpr int kSelectChunk = 128;     // blocks scored by one select workgroup
+constexpr int kSelectThreads = 256;
+
+}  // namespace sv

@@ -1,0 +1,259 @@
+// Block selection: GQA-batched scoring of block representatives by the first draft
+// token's query, piecewise budget, and top-k with lowest-index tie-break
+// (tutorial page "Accelerate Speculative Decoding with Sparse Computation in
+// Verification", section "Core technique 1"; sciencestack page of arXiv 2512.21911,
+// Figure 1 caption).
+//
+// One launch. Grid = (ceil(NB / 128) chunks, Hkv, B); workgroup (c, g, b) scores
+// blocks [128c, 128c+128) of sequence b for KV head g, streaming the float32
+// representatives through the block table (one 16-byte load per lane, D/4 lanes
+// per block, shuffle reduction in a fixed order). The last workgroup to finish for
+// (b, g) -- found with an arrival counter -- runs the budget and an LDS radix
+// select on order-preserving 32-bit keys, then compacts the chosen indices in
+// ascending order with block-wide scans. The counter is reset by that workgroup.
+#include "internal.h"
+
+namespace sv {
+namespace {
+
+constexpr int NT = kSelectThreads;
+constexpr int NWAVE = NT / 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Order-preserving map of a float score to an unsigned key: larger score, larger
+// key. -0 and +0 map to the same key; NaN maps to the key of -inf (the lowest
+// rank, tied with -inf). Key 0 is reserved for "not a candidate".
+__device__ __forceinline__ uint32_t score_key(float s) {
+  if (s != s) s = -__builtin_inff();
+  if (s == 0.0f) s = 0.0f;
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide exclusive scan of one int per thread; returns the prefix and sets
+// *total. Uses `scratch` (NWAVE ints of LDS). Must be called by all threads.
+__device__ int block_exclusive_scan(int v, int* total, int* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    const int t = scratch[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  *total = all;
+  return before + x - v;
+}
+
+__device__ __forceinline__ int budget_blocks_dev(const SelectParams& p, int ctx, int nb) {
+  if (ctx <= p.dense_ctx) return nb;
+  int k = (p.frac_per_mille * nb + 999) / 1000;
+  if (k < p.min_blocks) k = p.min_blocks;
+  return k < nb ? k : nb;
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
+  extern __shared__ uint32_t keys[];           // [NB] (top-k phase only)
+  __shared__ int hist[256];
+  __shared__ int scan_scratch[NWAVE];
+  __shared__ int bcast[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int unit = b * p.Hkv + g;
+  int ctx = p.ctx_lens[b];
+  if (ctx < 0) ctx = 0;
+  int nb = (ctx + p.bs - 1) / p.bs;
+  if (nb > p.NB) nb = p.NB;
+  float* sc = p.scores + static_cast<int64_t>(unit) * p.NB;
+  const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.NB;
+
+  // ------------------------------------------------------------ scoring
+  constexpr int LPB = D / 4;                   // lanes per block (one float4 each)
+  constexpr int BPW = 64 / LPB;                // blocks per wave per pass
+  constexpr int PASSES = kSelectChunk / (NWAVE * BPW);
+  const int sub = lane / LPB;
+  const int li = lane % LPB;
+  const int j0 = static_cast<int>(blockIdx.x) * kSelectChunk;
+  // A sequence whose budget keeps every block needs no scores.
+  const bool dense = budget_blocks_dev(p, ctx, nb) >= nb;
+  if (j0 < nb && (!dense || p.scores_requested)) {
+    const E* q = static_cast<const E*>(p.q) + static_cast<int64_t>(b) * p.T * p.Hq * D;
+    float qs[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int hl = 0; hl < p.G; ++hl) {
+      const E* qh = q + static_cast<int64_t>(g * p.G + hl) * D + 4 * li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v;
+        if constexpr (sizeof(E) == 2) v = bf16_to_f32(qh[e]); else v = qh[e];
+        qs[e] += v;
+      }
+    }
+    float4 r[PASSES];
+    int jj[PASSES];
+#pragma unroll
+    for (int u = 0; u < PASSES; ++u) {
+      const int j = j0 + (u * NWAVE + wave) * BPW + sub;
+      jj[u] = j;
+      r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < nb) {
+        const int phys = bt[j];
+        if (phys >= 0 && phys < p.P)
+          r[u] = *reinterpret_cast<const float4*>(
+              p.repr_pool + (static_cast<int64_t>(phys) * p.Hkv + g) * D + 4 * li);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PASSES; ++u) {
+      float d = qs[0] * r[u].x;
+      d = __builtin_fmaf(qs[1], r[u].y, d);
+      d = __builtin_fmaf(qs[2], r[u].z, d);
+      d = __builtin_fmaf(qs[3], r[u].w, d);
+#pragma unroll
+      for (int off = LPB / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off, 64);
+      if (li == 0 && jj[u] < nb) sc[jj[u]] = d;
+    }
+  }
+
+  // ------------------------------------------------------------ arrival
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = atomicAdd(p.tickets + unit, 1u);
+    bcast[0] = (prev == gridDim.x - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!bcast[0]) return;
+  __threadfence();
+
+  // ------------------------------------------------------------ budget + top-k
+  int k = budget_blocks_dev(p, ctx, nb);
+  if (k > p.k_max) k = p.k_max;
+  int32_t* out = p.idx + static_cast<int64_t>(unit) * p.k_max;
+  if (tid == 0) p.tickets[unit] = 0u;
+  if (k >= nb) {
+    if (tid == 0) p.cnt[unit] = nb;
+    for (int pos = tid; pos < p.k_max; pos += NT) out[pos] = pos < nb ? pos : -1;
+    return;
+  }
+  const int f0 = p.keep_first ? 0 : -1;
+  const int f1 = p.keep_last ? nb - 1 : -1;
+  const int nforced = (f0 >= 0) + (f1 >= 0 && f1 != f0);
+  int want = k - nforced;                     // candidates to pick
+  if (want < 0) want = 0;                     // k_max below the forced count: forced only
+
+  const int E_PER = (nb + NT - 1) / NT;       // contiguous keys owned by each thread
+  const int my_lo = tid * E_PER;
+  const int my_hi = my_lo + E_PER < nb ? my_lo + E_PER : nb;
+  for (int j = my_lo; j < my_hi; ++j) {
+    const bool forced = (j == f0) || (j == f1);
+    const float s = __hip_atomic_load(sc + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    keys[j] = forced ? 0u : score_key(s);
+  }
+  __syncthreads();
+
+  // Radix select of the want-th largest key: after 4 passes `prefix` is the
+  // threshold key and `want` the number of keys equal to it that are taken.
+  uint32_t prefix = 0u, mask = 0u;
+  if (want == 0) {
+    prefix = 0xFFFFFFFFu;                     // nothing beats it, no ties taken
+  } else {
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hist[tid] = 0;
+      __syncthreads();
+      for (int j = my_lo; j < my_hi; ++j) {
+        const uint32_t key = keys[j];
+        if (key != 0u && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      const int v = hist[255 - tid];
+      int tot;
+      const int cum = block_exclusive_scan(v, &tot, scan_scratch) + v;   // count of digits >= 255-tid
+      if (cum >= want && cum - v < want) {
+        bcast[1] = 255 - tid;
+        bcast[2] = want - (cum - v);
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(bcast[1]) << shift;
+      mask |= 255u << shift;
+      want = bcast[2];
+      __syncthreads();
+    }
+  }
+
+  // Ties at the threshold go to the lowest indices: rank equal keys in index order.
+  int n_eq = 0;
+  for (int j = my_lo; j < my_hi; ++j) n_eq += (keys[j] == prefix);
+  int tot;
+  const int eq_before = block_exclusive_scan(n_eq, &tot, scan_scratch);
+  int n_sel = 0;
+  {
+    int e = eq_before;
+    for (int j = my_lo; j < my_hi; ++j) {
+      const uint32_t key = keys[j];
+      const bool take = (j == f0) || (j == f1) || (key != 0u && key > prefix) ||
+                        (key == prefix && e < want);
+      e += (key == prefix);
+      n_sel += take;
+    }
+  }
+  int total_sel;
+  const int sel_before = block_exclusive_scan(n_sel, &total_sel, scan_scratch);
+  {
+    int e = eq_before;
+    int pos = sel_before;
+    for (int j = my_lo; j < my_hi; ++j) {
+      const uint32_t key = keys[j];
+      const bool take = (j == f0) || (j == f1) || (key != 0u && key > prefix) ||
+                        (key == prefix && e < want);
+      e += (key == prefix);
+      if (take) {
+        if (pos < p.k_max) out[pos] = j;
+        ++pos;
+      }
+    }
+  }
+  if (total_sel > p.k_max) total_sel = p.k_max;
+  if (tid == 0) p.cnt[unit] = total_sel;
+  for (int pos = total_sel + tid; pos < p.k_max; pos += NT) out[pos] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectParams& p, bool bf16, hipStream_t stream) {
+  if (p.B == 0) return hipSuccess;
+  dim3 grid((p.NB + kSelectChunk - 1) / kSelectChunk, p.Hkv, p.B);
+  const size_t lds = static_cast<size_t>(p.NB) * sizeof(uint32_t);
+  if (bf16) {
+    if (p.D == 128)
+      hipLaunchKernelGGL((select_kernel<uint16_t, 128>), grid, dim3(NT), lds, stream, p);
+    else
+      hipLaunchKernelGGL((select_kernel<uint16_t, 64>), grid, dim3(NT), lds, stream, p);
+  } else {
+    if (p.D == 128)
+      hipLaunchKernelGGL((select_kernel<float, 128>), grid, dim3(NT), lds, stream, p);
+    else
+      hipLaunchKernelGGL((select_kernel<float, 64>), grid, dim3(NT), lds, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sv

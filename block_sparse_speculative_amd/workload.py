@@ -1,0 +1,129 @@
+"""A resident instance of a workload: per-layer queries, draft K/V and paged KV pools
+built on the device through sv_block_repr, plus the index/output buffers of a pass.
+
+A verification pass over the instance runs, for every layer, either block selection
+(sv_select_blocks) or inter-layer reuse (sv_reuse_indices), then the sparse
+multi-draft attention (sv_sparse_verify_attn).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import torch
+
+from . import _lib as L
+from . import pipeline as PL
+from . import synth
+
+
+@dataclasses.dataclass
+class Layer:
+    q: torch.Tensor
+    k_draft: torch.Tensor
+    v_draft: torch.Tensor
+    pool: PL.Pool
+    reuse: bool
+    idx: torch.Tensor
+    cnt: torch.Tensor
+    out: torch.Tensor
+    lse: Optional[torch.Tensor]
+
+
+class Instance:
+    def __init__(self, w: synth.Workload, seed: int = 0, device="cuda", num_layers: Optional[int] = None,
+                 ctx_lens: Optional[List[int]] = None, paged: Optional[bool] = None,
+                 num_splits: int = 0, with_lse: bool = True, nan_pool: bool = False,
+                 k_max: Optional[int] = None, append_chunk: int = 0):
+        if paged is not None:
+            w = w.with_(paged=paged)
+        self.w = w
+        self.seed = seed
+        self.device = torch.device(device)
+        self.ctx_lens = list(ctx_lens) if ctx_lens is not None else synth.context_lengths(w, seed)
+        table, P = synth.block_table(w, self.ctx_lens, seed)
+        self.table_host = table
+        self.table = table.to(self.device)
+        self.ctx = torch.tensor(self.ctx_lens, dtype=torch.int32, device=self.device)
+        self.shape = L.make_shape(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                  w.block_size, table.shape[1], P, w.num_draft, w.torch_dtype)
+        self.budget = L.make_budget(*w.budget)
+        need = max([L.budget_blocks(self.budget, c, w.block_size) for c in self.ctx_lens] + [1])
+        self.k_max = max(need, k_max or 0)
+        self.scale = synth.softmax_scale(w)
+        self.ws = PL.Workspaces(self.shape, self.k_max, num_splits, self.device)
+        self.num_splits = L.attn_num_splits(self.shape, self.k_max, num_splits)
+        n_layers = w.num_layers if num_layers is None else num_layers
+        B, T, Hq, Hkv, D = w.num_seqs, w.num_draft, w.num_q_heads, w.num_kv_heads, w.head_dim
+        self.layers: List[Layer] = []
+        for l in range(n_layers):
+            x = synth.make_layer(w, seed, l, self.device, self.ctx_lens)
+            pool = PL.alloc_pool(self.shape, self.device, fill_nan=nan_pool)
+            PL.fill_pool(self.shape, pool, x["k_ctx"], x["v_ctx"], self.ctx_lens, self.table,
+                         chunk=append_chunk)
+            reuse = w.reuse_odd_layers and l % 2 == 1
+            self.layers.append(Layer(
+                q=x["q"], k_draft=x["k_draft"], v_draft=x["v_draft"], pool=pool, reuse=reuse,
+                idx=torch.full((B, Hkv, self.k_max), -7, dtype=torch.int32, device=self.device),
+                cnt=torch.full((B, Hkv), -7, dtype=torch.int32, device=self.device),
+                out=torch.empty((B, T, Hq, D), dtype=w.torch_dtype, device=self.device),
+                lse=torch.empty((B, T, Hq), dtype=torch.float32, device=self.device)
+                if with_lse else None))
+            del x
+
+    def logical(self, layer: int):
+        """Regenerate layer `layer`'s logical (unpaged) inputs on the device."""
+        return synth.make_layer(self.w, self.seed, layer, self.device, self.ctx_lens)
+
+    def select_or_reuse(self, l: int, scores: Optional[torch.Tensor] = None):
+        ly = self.layers[l]
+        if ly.reuse:
+            prev = self.layers[l - 1]
+            L.reuse_indices(self.shape, self.k_max, prev.idx, prev.cnt, ly.idx, ly.cnt)
+        else:
+            PL.select(self.shape, self.budget, ly.q, ly.pool, self.table, self.ctx, self.k_max,
+                      ly.idx, ly.cnt, self.ws, scores=scores)
+
+    def attend(self, l: int):
+        ly = self.layers[l]
+        PL.attend(self.shape, ly.q, ly.k_draft, ly.v_draft, ly.pool, self.table, self.ctx, ly.idx,
+                  ly.cnt, self.k_max, self.scale, ly.out, self.ws, lse=ly.lse)
+
+    def run_layer(self, l: int):
+        self.select_or_reuse(l)
+        self.attend(l)
+
+    def step(self):
+        for l in range(len(self.layers)):
+            self.run_layer(l)
+
+    # --------------------------------------------------------------- accounting
+    def selected_tokens(self) -> int:
+        """Context tokens attended in one pass, summed over layers, sequences and
+        KV heads (host arithmetic on the budget and context lengths)."""
+        bs = self.w.block_size
+        total = 0
+        for c in self.ctx_lens:
+            nb = -(-c // bs)
+            k = L.budget_blocks(self.budget, c, bs)
+            if k >= nb:
+                toks = c
+            else:
+                # every sparse selection holds the last (possibly partial) block
+                toks = k * bs - (nb * bs - c if self.budget.keep_last else 0)
+            total += toks
+        return total * self.w.num_kv_heads * len(self.layers)
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes of selected K/V plus representatives scored in one pass."""
+        esz = 4 if self.w.dtype == "fp32" else 2
+        kv = self.selected_tokens() * self.w.head_dim * 2 * esz
+        bs = self.w.block_size
+        select_layers = sum(1 for ly in self.layers if not ly.reuse)
+        reps = sum(-(-c // bs) for c in self.ctx_lens) * self.w.num_kv_heads * self.w.head_dim * 4
+        return kv + reps * select_layers
+
+    def units(self) -> int:
+        """Verified (draft token, query head) rows per pass, summed over layers."""
+        return self.w.num_seqs * self.w.num_draft * self.w.num_q_heads * len(self.layers)

@@ -1,0 +1,196 @@
+/*
+ * sv.h -- C ABI of the block-sparse multi-draft verification-attention library
+ * (libsv.so, MI355X / gfx950).
+ *
+ * The method (arXiv 2512.21911 as described on the tutorial page "Accelerate
+ * Speculative Decoding with Sparse Computation in Verification", section "Core
+ * technique 1", and on its sciencestack page, Figure 1 caption): during the
+ * verification pass of speculative decoding, every KV block carries a
+ * representative key; the first draft token's query scores the representatives;
+ * a piecewise budget keeps the top-k blocks; every draft token then attends over
+ * the shared selected blocks plus the draft tokens up to itself; a layer may reuse
+ * the previous layer's selection.
+ *
+ * Conventions for every entry point
+ *  - Buffer pointers are DEVICE pointers unless stated otherwise. The caller
+ *    allocates and owns every buffer, including workspaces. The library never
+ *    allocates or frees device memory, never synchronises, and keeps no pointer
+ *    after returning.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is
+ *    enqueued asynchronously on it, in call order.
+ *  - Every entry point returns an sv_status. Arguments visible to the host are
+ *    validated BEFORE anything is enqueued: a nonzero status means nothing was
+ *    launched. sv_last_error() then holds a message (thread-local).
+ *  - Values that live on the device (context lengths, block-table entries,
+ *    indices) are preconditions the host cannot check. Kernels skip entries outside
+ *    their valid range instead of reading out of bounds; results for such inputs
+ *    are unspecified.
+ *  - Tensor layouts are dense row-major with the shapes given below.
+ *      B   = num_seqs             Hq = num_q_heads      Hkv = num_kv_heads
+ *      G   = Hq / Hkv (GQA group; query head h uses KV head h / G)
+ *      D   = head_dim             bs = block_size       T  = num_draft
+ *      NB  = max_blocks_per_seq   P  = num_phys_blocks
+ *  - Paged KV pool (one pool per layer):
+ *      k_pool    [P, Hkv, bs, D]  element type `dtype` (token-major in a block)
+ *      v_pool    [P, Hkv, D, bs]  element type `dtype` (dim-major in a block)
+ *      repr_pool [P, Hkv, D]      float32, mean key of each block
+ *    block_table [B, NB] int32 maps logical block j of sequence b to a physical
+ *    block; only entries j < ceil(ctx_b / bs) are read.
+ *
+ * Supported envelope (else SV_ERR_UNSUPPORTED): D in {64, 128}; bs in {32, 64, 128};
+ * 1 <= T <= 16; T*G <= 128; dtype in {SV_F32, SV_BF16}; NB <= 16384.
+ */
+#ifndef SV_H_
+#define SV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+typedef enum sv_status {
+  SV_OK = 0,
+  SV_ERR_NULL_ARG = 1,     /* a required pointer is NULL                         */
+  SV_ERR_BAD_SHAPE = 2,    /* sizes inconsistent or out of range                  */
+  SV_ERR_UNSUPPORTED = 3,  /* outside the supported envelope                      */
+  SV_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required          */
+  SV_ERR_HIP = 5           /* a HIP launch or runtime call failed                 */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Problem sizes shared by all entry points (see the size names above). */
+typedef struct sv_shape {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t num_phys_blocks;
+  int32_t num_draft;
+  int32_t dtype;           /* sv_dtype */
+} sv_shape;
+
+/* Piecewise block budget (tutorial page, "Core technique 1": a large budget for
+ * short contexts and aggressive sparsity for long ones). With nb = ceil(ctx/bs):
+ *   k = nb                                                    if ctx <= dense_ctx_tokens
+ *   k = min(nb, max(min_blocks, ceil(frac_per_mille * nb / 1000)))   otherwise.
+ * keep_first / keep_last force block 0 and block nb-1 into every sparse
+ * selection; forced blocks count inside k. Requires dense_ctx_tokens >= 0,
+ * 0 <= frac_per_mille <= 1000 and min_blocks >= keep_first + keep_last. */
+typedef struct sv_budget {
+  int32_t dense_ctx_tokens;
+  int32_t min_blocks;
+  int32_t frac_per_mille;
+  int32_t keep_first;
+  int32_t keep_last;
+} sv_budget;
+
+/* Library ABI version (SV_ABI_VERSION of the build). */
+int32_t sv_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* sv_status_str(int32_t status);
+
+/* Message describing the last failure of an entry point on this thread ("" if
+ * none). Valid until the next call into the library on this thread. */
+const char* sv_last_error(void);
+
+/* Host-only, pure: the block budget k for one sequence (formula in sv_budget).
+ * Returns -1 if `budget` is NULL or invalid, or if ctx_len < 0 or block_size <= 0. */
+int32_t sv_budget_blocks(const sv_budget* budget, int32_t ctx_len, int32_t block_size);
+
+/* KV append fused with the block-representative update (representative value of a
+ * block: sciencestack page, Figure 1 caption; the pages leave it undefined and this
+ * library takes the arithmetic mean of the block's keys over its valid tokens).
+ *
+ * For each sequence b, the n_new[b] tokens k_new[b, 0:n_new[b]] / v_new[...] are
+ * written at logical positions ctx_before[b] .. ctx_before[b]+n_new[b]-1 of the
+ * pool through block_table. Then, for every block touched, repr_pool receives the
+ * float32 mean of ALL its valid keys (old and new), summed in slot order, so a
+ * block's representative does not depend on how its tokens arrived.
+ *   k_new, v_new  [B, n_new_max, Hkv, D]  dtype
+ *   n_new         [B] int32, 0 <= n_new[b] <= n_new_max      (device)
+ *   ctx_before    [B] int32, ctx_before[b]+n_new[b] <= NB*bs (device)
+ *   block_table   [B, NB] int32                              (device)
+ *   k_pool, v_pool, repr_pool  pool tensors (layouts above), updated in place.
+ * n_new_max may be 0 (nothing is launched). */
+sv_status sv_block_repr(const sv_shape* shape, const void* k_new, const void* v_new,
+                        int32_t n_new_max, const int32_t* n_new, const int32_t* ctx_before,
+                        const int32_t* block_table, void* k_pool, void* v_pool,
+                        float* repr_pool, void* stream);
+
+/* Bytes of workspace sv_select_blocks needs for this shape. */
+size_t sv_select_workspace_bytes(const sv_shape* shape, int32_t k_max);
+
+/* Block selection: GQA-batched scoring + piecewise budget + top-k
+ * (tutorial page, "Core technique 1"; sciencestack page, Figure 1 caption: the
+ * first draft token's query against each block representative, one shared set).
+ *
+ * For sequence b and KV head g, with nb = ceil(ctx_lens[b]/bs):
+ *   score[j] = sum over the G query heads h of g of  q[b,0,h,:] . repr_pool[bt[b,j], g, :]
+ * computed in float32 (unscaled). k = budget(ctx_lens[b]). If k >= nb every block
+ * is selected; otherwise the forced blocks plus the k - |forced| best other blocks
+ * by score (ties to the lower index; NaN ranks lowest).
+ *   q          [B, T, Hq, D] dtype; only draft token 0 is read
+ *   idx        [B, Hkv, k_max] int32 out: ascending logical indices, padded with -1
+ *   cnt        [B, Hkv]        int32 out: number of selected blocks (= k)
+ *   scores     [B, Hkv, NB]    float32 out, optional (NULL): the block scores
+ * k_max must be >= k for every sequence (use sv_budget_blocks); a larger k is
+ * clamped to k_max. `ws` must hold sv_select_workspace_bytes() bytes, must be
+ * zero-filled before its first use, and is left zero-filled by every call that
+ * completes; do not share it with other entry points or with concurrent calls. */
+sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const void* q,
+                           const float* repr_pool, const int32_t* block_table,
+                           const int32_t* ctx_lens, int32_t k_max, int32_t* idx,
+                           int32_t* cnt, float* scores, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Number of KV splits sv_sparse_verify_attn uses: `num_splits` if > 0 (clamped to
+ * the work available), else the library's choice for this shape. */
+int32_t sv_attn_num_splits(const sv_shape* shape, int32_t k_max, int32_t num_splits);
+
+/* Bytes of workspace sv_sparse_verify_attn needs (0 when one split is used). */
+size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num_splits);
+
+/* Multi-draft attention over the shared selected blocks (sciencestack page,
+ * Figure 1 caption: all draft tokens use the same selected block set; abstract:
+ * draft tokens are verified in one parallel pass).
+ *
+ * Draft token t of query head h (KV head g = h / G) attends over every valid
+ * context token of the blocks idx[b, g, 0:cnt[b,g]] and over draft tokens 0..t:
+ *   out[b,t,h,:] = softmax_k(scale * q[b,t,h,:] . key_k) @ value_k
+ *   lse[b,t,h]   = natural log of the softmax denominator (of the scaled logits)
+ * Accumulation is float32; `out` is rounded to dtype (round to nearest even).
+ *   q                 [B, T, Hq, D]   dtype
+ *   k_draft, v_draft  [B, T, Hkv, D]  dtype (the draft tokens' own keys/values)
+ *   k_pool, v_pool, block_table      as above
+ *   ctx_lens [B] int32; idx [B, Hkv, k_max]; cnt [B, Hkv]   (device)
+ *   out [B, T, Hq, D] dtype; lse [B, T, Hq] float32 or NULL
+ * num_splits: 0 = library choice, else the number of KV splits (see
+ * sv_attn_num_splits). `ws` must hold sv_attn_workspace_bytes() bytes (may be
+ * NULL when that is 0); its contents need no initialisation. */
+sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,
+                                const void* v_draft, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* ctx_lens,
+                                const int32_t* idx, const int32_t* cnt, int32_t k_max,
+                                float scale, int32_t num_splits, void* out, float* lse,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Inter-layer retrieval reuse (tutorial page, "Core technique 1": some layers take
+ * the previous layer's retrieval result instead of selecting again; sciencestack
+ * abstract: inter-layer retrieval reuse). Copies prev_idx [B, Hkv, k_max] and
+ * prev_cnt [B, Hkv] into idx / cnt. The buffers must not overlap. */
+sv_status sv_reuse_indices(const sv_shape* shape, int32_t k_max, const int32_t* prev_idx,
+                           const int32_t* prev_cnt, int32_t* idx, int32_t* cnt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_H_ */

@@ -1,0 +1,165 @@
+"""C-ABI library tests that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid host-visible arguments before launching.
+
+Calls here that pass fake (non-null, never dereferenced) pointers always fail host
+validation first, so nothing reaches the GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_speculative_amd as sv
+from block_sparse_speculative_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
+                                reason="libsv.so not built (run __graft_entry__.build())")
+
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(sv.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sv.lib()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert sv.abi_version() == 1
+
+
+def test_status_strings():
+    lib = sv.lib()
+    assert lib.sv_status_str(0) == b"SV_OK"
+    assert lib.sv_status_str(4) == b"SV_ERR_WORKSPACE"
+    assert lib.sv_status_str(99) == b"SV_ERR_UNKNOWN"
+
+
+def _golden_budget_rows():
+    rows = []
+    with open(os.path.join(ROOT, "tests", "golden", "budget_table.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                rows.append(tuple(int(x) for x in line.split()))
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden_budget_rows())
+def test_host_budget_matches_hand_derived_table(row):
+    ctx, bs, dense, mn, frac, expected = row
+    assert sv.budget_blocks(sv.make_budget(dense, mn, frac), ctx, bs) == expected
+
+
+def test_budget_rejects_invalid():
+    assert sv.budget_blocks(sv.make_budget(0, 1, 0, 1, 1), 100, 64) == -1      # min < forced
+    assert sv.budget_blocks(sv.make_budget(0, 4, 1001), 100, 64) == -1
+    assert sv.budget_blocks(sv.make_budget(0, 4, 10), -1, 64) == -1
+    assert sv.budget_blocks(sv.make_budget(0, 4, 10), 10, 0) == -1
+
+
+def _shape(**kw):
+    base = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=64,
+                max_blocks_per_seq=1024, num_phys_blocks=2048, num_draft=8, dtype=sv.SV_BF16)
+    base.update(kw)
+    return L.Shape(**base)
+
+
+def _attn(shape, k_max=64, ws=None, ws_bytes=0, out=FAKE, scale=0.1, splits=0):
+    lib = sv.lib()
+    return lib.sv_sparse_verify_attn(ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, k_max, scale, splits, out, None, ws, ws_bytes,
+                                     None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 3), (dict(block_size=16), 3), (dict(num_q_heads=30), 2),
+    (dict(num_draft=17), 3), (dict(num_draft=0), 2), (dict(dtype=7), 3),
+    (dict(num_q_heads=64, num_kv_heads=4, num_draft=16), 3),   # T*G = 256 > 128
+    (dict(max_blocks_per_seq=20000), 3), (dict(num_phys_blocks=0), 2), (dict(num_seqs=-1), 2),
+])
+def test_attention_rejects_shapes_before_launch(kw, status):
+    assert _attn(_shape(**kw)) == status
+    assert sv.lib().sv_last_error() != b""
+
+
+def test_attention_rejects_workspace_null_args_and_kmax():
+    shape = _shape()
+    need = sv.attn_workspace_bytes(shape, 64)
+    assert need > 0 and sv.attn_num_splits(shape, 64) > 1
+    assert _attn(shape, ws=None, ws_bytes=0) == 4
+    assert _attn(shape, ws=FAKE, ws_bytes=need - 1) == 4
+    assert _attn(shape, out=None, ws=FAKE, ws_bytes=need) == 1
+    assert _attn(shape, k_max=0) == 2
+    assert _attn(shape, k_max=2000) == 2
+    assert _attn(shape, scale=float("nan")) == 2
+    assert _attn(shape, splits=-3) == 2
+
+
+def test_split_count_and_workspace_size():
+    shape = _shape(num_seqs=1)
+    assert sv.attn_num_splits(shape, 64, 1) == 1
+    assert sv.attn_workspace_bytes(shape, 64, 1) == 0
+    assert sv.attn_num_splits(shape, 64, 10_000) == 64          # clamped to the context tiles
+    s4 = sv.attn_num_splits(shape, 64, 4)
+    rows, d, units = 8 * 4, 128, 8
+    assert s4 == 4
+    assert sv.attn_workspace_bytes(shape, 64, 4) >= units * 4 * rows * (d + 2) * 4
+    # bs 128 uses two 64-token tiles per block
+    assert sv.attn_num_splits(_shape(num_seqs=1, block_size=128), 64, 10_000) == 128
+
+
+def test_select_rejects_bad_budget_and_workspace():
+    lib = sv.lib()
+    shape = _shape()
+
+    def call(budget, ws=FAKE, ws_bytes=1 << 30, k_max=64, q=FAKE):
+        return lib.sv_select_blocks(ctypes.byref(shape), budget, q, FAKE, FAKE, FAKE, k_max, FAKE,
+                                    FAKE, None, ws, ws_bytes, None)
+
+    good = ctypes.byref(sv.make_budget(4096, 64, 50))
+    assert call(None) == 1
+    assert call(ctypes.byref(sv.make_budget(4096, 1, 50, 1, 1))) == 2
+    assert call(ctypes.byref(sv.make_budget(4096, 64, 2000))) == 2
+    assert call(ctypes.byref(sv.make_budget(-1, 64, 50))) == 2
+    assert call(good, ws=None, ws_bytes=0) == 4
+    need = sv.select_workspace_bytes(shape, 64)
+    assert need >= 2 * 8 * 1024 * 4
+    assert call(good, ws_bytes=need - 1) == 4
+    assert call(good, q=None) == 1
+    assert call(good, k_max=0) == 2
+
+
+def test_repr_and_reuse_reject_before_launch():
+    lib = sv.lib()
+    shape = _shape()
+    assert lib.sv_block_repr(ctypes.byref(shape), None, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, None) == 1
+    assert lib.sv_block_repr(ctypes.byref(shape), FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, None) == 2
+    assert lib.sv_block_repr(ctypes.byref(_shape(head_dim=32)), FAKE, FAKE, 4, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, FAKE, None) == 3
+    assert lib.sv_reuse_indices(ctypes.byref(shape), 64, None, FAKE, FAKE, FAKE, None) == 1
+    # overlapping source and destination
+    assert lib.sv_reuse_indices(ctypes.byref(shape), 64, FAKE, ctypes.c_void_p(0x900000), FAKE,
+                                ctypes.c_void_p(0xA00000), None) == 2
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    shape = _shape(num_seqs=1)
+    t = torch.zeros(1, 8, 8, 64, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sv.reuse_indices(shape, 64, t, t, t, t)

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
+
+Small workloads are checked on every (sequence, KV head) unit; the full-size
+workloads are checked on sampled units, in the launch configuration the bench times
+(library-chosen split count). Selected indices must be exact except inside the
+near-tie band; outputs must meet the fp32 / bf16 tolerances (tests/parity.py).
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_speculative_amd import synth
+from block_sparse_speculative_amd.workload import Instance
+
+import parity as PT
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _all_units(inst):
+    return [(b, g) for b in range(inst.w.num_seqs) for g in range(inst.w.num_kv_heads)]
+
+
+def run_and_check(inst, units=None, layers=None, check_reps=True, scores=False):
+    """Run one pass of `inst` and check the listed units of the listed layers."""
+    n = len(inst.layers)
+    layers = list(range(n)) if layers is None else layers
+    units = _all_units(inst) if units is None else units
+    gscores = None
+    for l in range(n):
+        if scores and not inst.layers[l].reuse:
+            gscores = torch.full((inst.w.num_seqs, inst.w.num_kv_heads, inst.shape.max_blocks_per_seq),
+                                 float("nan"), dtype=torch.float32, device=inst.device)
+            inst.select_or_reuse(l, scores=gscores)
+        else:
+            inst.select_or_reuse(l)
+        inst.attend(l)
+    torch.cuda.synchronize()
+    prev, stats_all = None, []
+    for l in layers:
+        ly = inst.layers[l]
+        p = prev if ly.reuse else None
+        if ly.reuse and prev is None:
+            # the selecting layer before a reuse layer must be checked first
+            p, _ = PT.verify_instance_units(inst, l - 1, units, check_reps_too=False)
+        sels, st = PT.verify_instance_units(inst, l, units, prev_sel=p,
+                                            check_reps_too=check_reps and not ly.reuse,
+                                            gpu_scores=gscores if (scores and not ly.reuse) else None)
+        PT.log(f"  layer {l} ({'reuse' if ly.reuse else 'select'}): {st}")
+        prev = sels
+        stats_all.append(st)
+    return stats_all
+
+
+# ------------------------------------------------------------------ small workloads
+
+SMALL = {
+    "tiny": W["tiny"],
+    "llama_small": W["llama32k"].with_(num_seqs=2, num_q_heads=8, num_kv_heads=2, ctx=(8192, 6000)),
+    "qwen_small": W["qwen128k"].with_(num_seqs=1, num_q_heads=16, num_kv_heads=2, ctx=(40000,)),
+    "ragged_small": W["ragged"].with_(num_seqs=3, num_q_heads=8, num_kv_heads=2,
+                                      ctx=(4096, 5000, 9000), ctx_range=None),
+    "rows64": W["llama32k"].with_(num_q_heads=16, num_kv_heads=2, ctx=(7000,)),
+    "d64_bs32": W["llama32k"].with_(head_dim=64, block_size=32, num_draft=2, num_q_heads=16,
+                                    num_kv_heads=2, ctx=(3000,), budget=(0, 16, 100, 1, 1)),
+    "fp32_d128": W["tiny"].with_(head_dim=128, block_size=64, ctx=(5000,),
+                                 budget=(0, 12, 0, 1, 1), plant_count=4),
+    "fp32_rows32_bs128": W["tiny"].with_(num_draft=8, block_size=128, ctx=(4500,),
+                                         budget=(0, 8, 0, 1, 1)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("splits", [0, 1, 2, 1000])
+def test_small_workload_all_units(name, splits):
+    _gpu()
+    PT.log(f"[small] {name} splits={splits}")
+    inst = Instance(SMALL[name], seed=11, num_splits=splits, nan_pool=True)
+    PT.log(f"  resolved splits={inst.num_splits} k_max={inst.k_max}")
+    run_and_check(inst, scores=(splits == 0))
+    del inst
+    _free()
+
+
+def test_tiny_planted_blocks_selected():
+    _gpu()
+    inst = Instance(W["tiny"], seed=0)
+    inst.step()
+    torch.cuda.synchronize()
+    heavy = synth.planted_sets(inst.w, inst.ctx_lens, 0, 0)
+    idx, cnt = inst.layers[0].idx.cpu(), inst.layers[0].cnt.cpu()
+    for g in range(inst.w.num_kv_heads):
+        sel = PT.gpu_unit_selection(idx, cnt, 0, g)
+        assert len(sel) == 16 and set(heavy[0][g]) <= set(sel)
+
+
+# ------------------------------------------------------------------ edge cases
+
+EDGE = W["llama32k"].with_(num_seqs=4, num_q_heads=8, num_kv_heads=2, ctx=(0, 17, 200, 1000),
+                           budget=(0, 2, 0, 1, 1))
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_edge_contexts_empty_partial_forced_only(splits):
+    # ctx 0 (drafts only), one partial block, and sparse selections of forced blocks only
+    _gpu()
+    PT.log(f"[edge] contexts {EDGE.ctx} splits={splits}")
+    inst = Instance(EDGE, seed=3, num_splits=splits, nan_pool=True)
+    run_and_check(inst)
+
+
+def test_single_query_single_head_decode():
+    # T = 1, G = 1: plain single-query decode
+    _gpu()
+    w = W["llama32k"].with_(num_seqs=2, num_q_heads=4, num_kv_heads=4, num_draft=1,
+                            ctx=(3000, 9000), budget=(4096, 64, 50, 1, 1))
+    inst = Instance(w, seed=5, nan_pool=True)
+    run_and_check(inst)
+
+
+@pytest.mark.parametrize("flags", [(0, 0), (1, 0), (0, 1)])
+def test_forced_block_flags(flags):
+    _gpu()
+    w = W["llama32k"].with_(num_seqs=1, num_q_heads=8, num_kv_heads=2, ctx=(6000,),
+                            budget=(0, 5, 0) + flags)
+    run_and_check(Instance(w, seed=9, nan_pool=True))
+
+
+def test_k_max_larger_than_budget_pads_with_minus_one():
+    _gpu()
+    w = W["llama32k"].with_(num_seqs=2, num_q_heads=8, num_kv_heads=2, ctx=(5000, 300),
+                            budget=(0, 16, 0, 1, 1))
+    inst = Instance(w, seed=2, k_max=40, nan_pool=True)
+    run_and_check(inst)
+    cnt = inst.layers[0].cnt.cpu()
+    assert cnt[0].tolist() == [16, 16] and cnt[1].tolist() == [5, 5]
+
+
+# ------------------------------------------------------------------ invariances
+
+def _outputs(inst):
+    inst.step()
+    torch.cuda.synchronize()
+    ly = inst.layers[0]
+    return ly.idx.cpu().clone(), ly.out.float().cpu().clone(), ly.lse.cpu().clone()
+
+
+def test_run_to_run_bit_identical():
+    _gpu()
+    inst = Instance(SMALL["llama_small"], seed=21)
+    a = _outputs(inst)
+    b = _outputs(inst)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_paged_and_contiguous_tables_bit_identical():
+    _gpu()
+    w = SMALL["ragged_small"]
+    a = _outputs(Instance(w, seed=4, paged=True))
+    b = _outputs(Instance(w, seed=4, paged=False))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_incremental_append_matches_bulk_bit_identical():
+    # tokens appended in odd-sized chunks give the same pool and representatives
+    _gpu()
+    w = SMALL["llama_small"]
+    bulk = Instance(w, seed=8)
+    inc = Instance(w, seed=8, append_chunk=37)
+    table = bulk.table_host
+    for b, c in enumerate(bulk.ctx_lens):
+        nb = -(-c // w.block_size)
+        phys = table[b, :nb].to(bulk.device).long()
+        pa, pb = bulk.layers[0].pool, inc.layers[0].pool
+        assert torch.equal(pa.reps[phys], pb.reps[phys])
+        full = c // w.block_size
+        if full:
+            assert torch.equal(pa.k[phys[:full]], pb.k[phys[:full]])
+            assert torch.equal(pa.v[phys[:full]], pb.v[phys[:full]])
+
+
+def test_split_counts_agree_within_tolerance():
+    _gpu()
+    w = SMALL["qwen_small"]
+    outs = []
+    for s in (1, 2, 7, 1000):
+        _, o, _ = _outputs(Instance(w, seed=6, num_splits=s))
+        outs.append(o)
+    for o in outs[1:]:
+        assert (o - outs[0]).abs().max().item() <= 1e-2
+
+
+def test_stack_with_reuse_small():
+    _gpu()
+    w = W["stack64k"].with_(num_seqs=2, num_q_heads=8, num_kv_heads=2, ctx=(8192, 7000))
+    inst = Instance(w, seed=13, num_layers=4, nan_pool=True)
+    run_and_check(inst)
+
+
+# ------------------------------------------------------------------ full sizes
+
+def test_full_llama32k_all_units():
+    _gpu()
+    PT.log("[full] llama32k")
+    inst = Instance(W["llama32k"], seed=1)
+    run_and_check(inst)
+    del inst
+    _free()
+
+
+def test_full_ragged_sampled_units():
+    _gpu()
+    PT.log("[full] ragged")
+    inst = Instance(W["ragged"], seed=2)
+    lens = inst.ctx_lens
+    bs = [int(np.argmin(lens)), int(np.argmax(lens)), 5, 11]
+    units = sorted({(b, g) for b, g in zip(bs, [0, 7, 3, 5])})
+    PT.log(f"  ctx_lens={lens} units={units}")
+    run_and_check(inst, units=units)
+    del inst
+    _free()
+
+
+def test_full_qwen128k_all_units():
+    _gpu()
+    PT.log("[full] qwen128k")
+    inst = Instance(W["qwen128k"], seed=4)
+    run_and_check(inst, check_reps=False)
+    del inst
+    _free()
+
+
+def test_full_stack64k_sampled_layers_and_units():
+    _gpu()
+    PT.log("[full] stack64k (32 layers)")
+    inst = Instance(W["stack64k"], seed=3)
+    run_and_check(inst, units=[(0, 0), (3, 7), (2, 4)], layers=[0, 1, 30, 31], check_reps=False)
+    del inst
+    _free()
