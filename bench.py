@@ -1,0 +1,275 @@
+"""Throughput of the block-sparse multi-draft verification hot path on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stack64k]
+
+A step is one verification pass over the whole workload: for every layer, block
+selection (sv_select_blocks) or inter-layer reuse (sv_reuse_indices), then sparse
+multi-draft attention (sv_sparse_verify_attn). Inputs are seeded synthetic tensors
+already resident in HBM (the paged KV pools are built with sv_block_repr before
+timing). The step is captured once in a HIP graph and replayed.
+
+Prints one JSON line. `value` is verified draft-token-heads per second (rows of
+(draft token, query head) per layer, summed over layers and sequences).
+`roofline` refers to the attention entry point (the dominant cost): algorithmic
+bytes (selected K/V of one layer) over its average duration, timed with HIP events
+on the stream it runs on. `cpu_baseline` times the fp64 oracle on a bounded sample of
+the same workload on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "verify-attn draft-token-heads/s and % HBM peak at 32K-128K ctx, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="stack64k")
+    ap.add_argument("--instances", type=int, default=0,
+                    help="rotated resident copies (0: enough to exceed the 256 MB last-level cache)")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration(mib: int, reps: int):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters
+    (FETCH_SIZE / WRITE_SIZE) read by the profiler."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_mib": mib, "reps": reps, "bytes_read_per_copy": n * 4,
+                      "bytes_written_per_copy": n * 4, "gbs": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
+def cpu_baseline(inst, budget_s: float):
+    """Oracle draft-token-heads/s on host cores, on whole layers of one sequence of the
+    same workload, until about `budget_s` seconds of oracle work. Representatives are
+    computed outside the timed region (they exist before verification)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    w = inst.w
+    G, bs, T = w.group, w.block_size, w.num_draft
+    dense, mn, frac, kf, kl = w.budget
+    b = 0
+    ctx = inst.ctx_lens[b]
+    timed, rows, layers_done, units_done = 0.0, 0, 0, 0
+    prev = None
+    with threadpool_limits(limits=1):
+        for l in range(len(inst.layers)):
+            x = inst.logical(l)
+            q = x["q"][b].float().cpu().numpy()
+            kc = x["k_ctx"][b, :ctx].float().cpu().numpy()
+            vc = x["v_ctx"][b, :ctx].float().cpu().numpy()
+            kd = x["k_draft"][b].float().cpu().numpy()
+            vd = x["v_draft"][b].float().cpu().numpy()
+            del x
+            reuse = inst.layers[l].reuse
+            sels = []
+            for g in range(w.num_kv_heads):
+                sl = slice(g, g + 1)
+                qg = q[:, g * G:(g + 1) * G]
+                if not reuse:
+                    reps = O.block_representatives(kc[:, sl], bs)          # untimed
+                t0 = time.perf_counter()
+                if reuse:
+                    sel = prev[g]
+                else:
+                    sc = O.block_scores(qg[0], reps, G)[0]
+                    k = O.budget_blocks(ctx, bs, dense, mn, frac)
+                    sel = O.select_blocks(sc, k, bool(kf), bool(kl))
+                O.verify_attention(qg, kc[:, sl], vc[:, sl], kd[:, sl], vd[:, sl], [sel], bs,
+                                   inst.scale)
+                timed += time.perf_counter() - t0
+                sels.append(sel)
+                rows += T * G
+                units_done += 1
+            prev = sels
+            layers_done += 1
+            if timed >= budget_s and (not w.reuse_odd_layers or layers_done % 2 == 0):
+                break
+    return {
+        "value": rows / timed,
+        "unit": "draft-token-heads/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"sequence 0 (ctx {ctx}), layers 0..{layers_done - 1} of {len(inst.layers)}, "
+                   f"all {w.num_kv_heads} KV heads: {units_done} units, {rows} draft-token-heads, "
+                   f"{timed:.1f} s single-threaded numpy fp64 (scores, budget, top-k, attention; "
+                   f"representatives precomputed)"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the per-GPU "
+              f"share of a sharded deployment is the single-GPU workload measured here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, max(1, args.steps))
+        return
+
+    from block_sparse_speculative_amd import synth
+    from block_sparse_speculative_amd import workload as WL
+    from block_sparse_speculative_amd.workload import Instance
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = synth.WORKLOADS[args.workload]
+    # Rotate resident copies so one rotation touches more than 2 x 256 MB of
+    # selected data and representatives (the MI355X last-level cache).
+    bytes_per_pass = WL.algorithmic_bytes(w, synth.context_lengths(w, args.seed), w.num_layers)
+    reps_total = args.instances or max(1, -(-2 * 256 * 2 ** 20 // bytes_per_pass))
+    print(f"[bench] workload {w.name}: {bytes_per_pass / 1e6:.1f} MB algorithmic per pass, "
+          f"{reps_total} resident instance(s)", file=sys.stderr, flush=True)
+    def progress(done, total):
+        if done == total or done % 8 == 0:
+            print(f"[bench]   built layer {done}/{total}", file=sys.stderr, flush=True)
+
+    insts = [Instance(w, seed=args.seed + r, num_splits=args.num_splits, with_lse=False,
+                      progress=progress) for r in range(reps_total)]
+    inst0 = insts[0]
+    torch.cuda.synchronize()
+
+    def step():
+        for it in insts:
+            it.step()
+
+    use_graph = not args.no_graph
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        run = graph.replay
+    else:
+        run = step
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # The graph covers `reps_total` passes; a step is one pass.
+    passes = args.steps * reps_total
+    s_per_pass = wall / passes
+    units = inst0.units()
+    value = units / s_per_pass
+    step_gbs = bytes_per_pass / s_per_pass / 1e9
+
+    # ---- roofline of the attention entry point: a graph of only the attention calls
+    # of every layer (indices from the passes above), replayed between HIP events on
+    # the stream it runs on.
+    attn_graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for it in insts:
+            for l in range(len(it.layers)):
+                it.attend(l)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(attn_graph):
+        for it in insts:
+            for l in range(len(it.layers)):
+                it.attend(l)
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    attn_graph.replay()
+    stream.synchronize()
+    reps_attn = max(3, args.steps)
+    ev0.record(stream)
+    for _ in range(reps_attn):
+        attn_graph.replay()
+    ev1.record(stream)
+    ev1.synchronize()
+    launches = reps_attn * reps_total * len(inst0.layers)
+    attn_us = ev0.elapsed_time(ev1) * 1e3 / launches
+    kv_bytes_per_launch = (inst0.selected_tokens() // len(inst0.layers)) * w.head_dim * 2 * (
+        4 if w.dtype == "fp32" else 2)
+    achieved = kv_bytes_per_launch / (attn_us * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "draft-token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": s_per_pass * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian K/V/Q with planted heavy blocks; random-init, no weights)",
+        "config": {
+            "workload": w.name, "layers": len(inst0.layers), "num_seqs": w.num_seqs,
+            "ctx": inst0.ctx_lens if len(set(inst0.ctx_lens)) > 1 else inst0.ctx_lens[0],
+            "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "draft_tokens": w.num_draft, "k_max": inst0.k_max,
+            "reuse": "odd layers reuse" if w.reuse_odd_layers else "none",
+            "splits": inst0.num_splits, "graph": use_graph, "resident_instances": reps_total,
+        },
+        "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": bytes_per_pass,
+        "roofline": {
+            "kernel": "sv_sparse_verify_attn (attn_kernel + merge_kernel)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "avg_launch_us": attn_us,
+            "algorithmic_bytes_per_launch": kv_bytes_per_launch,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inst0, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -168,8 +168,8 @@ def block_repr(shape: Shape, k_new, v_new, n_new, ctx_before, block_table, k_poo
 
 def select_blocks(shape: Shape, budget: Budget, q, repr_pool, block_table, ctx_lens, k_max: int,
                   idx, cnt, scores=None, ws=None):
-    """sv_select_blocks. `ws` must be a zero-initialised uint8 device tensor of at least
-    select_workspace_bytes() bytes, reserved for selection calls."""
+    """sv_select_blocks. `ws` is a uint8 device tensor of at least
+    select_workspace_bytes() bytes."""
     B, Hq, Hkv, D, T = (shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim,
                         shape.num_draft)
     _dev(q, "q", _elem(shape), (B, T, Hq, D))

@@ -95,36 +95,41 @@ sv_status check_kmax(const sv_shape* s, int32_t k_max, const char* what) {
 }
 
 int resolve_splits(const sv_shape* s, int32_t k_max, int32_t num_splits) {
-  const int tt = sv::attn_tile_tokens(s->block_size);
+  const int tt = sv::attn_tile_tokens(s->block_size, s->dtype == SV_BF16);
   const int64_t ctx_tiles = static_cast<int64_t>(k_max) * (s->block_size / tt);
   int64_t want = num_splits;
   if (want <= 0) {
     const int64_t units = static_cast<int64_t>(s->num_seqs) * s->num_kv_heads;
-    const int64_t target_wgs = 256;
+    const int64_t target_wgs = 512;   // two attention workgroups per CU
     want = units > 0 ? (target_wgs + units - 1) / units : 1;
   }
   if (want > ctx_tiles) want = ctx_tiles;
+  // A split may straddle one block boundary at each end: keep it within the
+  // attention kernel's descriptor table.
+  const int64_t min_splits = (k_max + sv::kAttnMaxBlocksPerSplit - 2) / (sv::kAttnMaxBlocksPerSplit - 1);
+  if (want < min_splits) want = min_splits;
   if (want < 1) want = 1;
   return static_cast<int>(want);
 }
 
 size_t select_ws_layout(const sv_shape* s, size_t* scores_off) {
   const size_t units = static_cast<size_t>(s->num_seqs) * s->num_kv_heads;
-  const size_t tickets = align_up(units * sizeof(uint32_t));
-  *scores_off = tickets;
-  return tickets + align_up(units * s->max_blocks_per_seq * sizeof(float));
+  *scores_off = 0;
+  return align_up(units * s->max_blocks_per_seq * sizeof(float));
 }
 
-size_t attn_ws_layout(const sv_shape* s, int splits, size_t* ml_off) {
+// Attention workspace: [arrival counters: units x u32][partial O][partial (m, l)].
+size_t attn_ws_layout(const sv_shape* s, int splits, size_t* o_off, size_t* ml_off) {
   if (splits <= 1) {
-    *ml_off = 0;
+    *o_off = *ml_off = 0;
     return 0;
   }
   const size_t rows = static_cast<size_t>(s->num_draft) * (s->num_q_heads / s->num_kv_heads);
   const size_t units = static_cast<size_t>(s->num_seqs) * s->num_kv_heads;
-  const size_t o = align_up(units * splits * rows * s->head_dim * sizeof(float));
-  *ml_off = o;
-  return o + align_up(units * splits * rows * 2 * sizeof(float));
+  const size_t parts = static_cast<size_t>(splits) + 1;   // + the draft-only split
+  *o_off = align_up(units * sizeof(uint32_t));
+  *ml_off = *o_off + align_up(units * parts * rows * s->head_dim * sizeof(float));
+  return *ml_off + align_up(units * parts * rows * 2 * sizeof(float));
 }
 
 }  // namespace
@@ -216,7 +221,6 @@ sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const
   p.cnt = cnt;
   p.scores = scores ? scores : reinterpret_cast<float*>(w + scores_off);
   p.scores_requested = scores != nullptr;
-  p.tickets = reinterpret_cast<uint32_t*>(w);
   p.B = shape->num_seqs;
   p.Hq = shape->num_q_heads;
   p.Hkv = shape->num_kv_heads;
@@ -245,8 +249,8 @@ int32_t sv_attn_num_splits(const sv_shape* shape, int32_t k_max, int32_t num_spl
 size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num_splits) {
   if (check_shape(shape, "sv_attn_workspace_bytes") != SV_OK) return 0;
   if (check_kmax(shape, k_max, "sv_attn_workspace_bytes") != SV_OK) return 0;
-  size_t off;
-  return attn_ws_layout(shape, resolve_splits(shape, k_max, num_splits), &off);
+  size_t o_off, ml_off;
+  return attn_ws_layout(shape, resolve_splits(shape, k_max, num_splits), &o_off, &ml_off);
 }
 
 sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,
@@ -259,15 +263,15 @@ sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void
   if (sv_status st = check_shape(shape, what)) return st;
   if (sv_status st = check_kmax(shape, k_max, what)) return st;
   if (num_splits < 0) return fail(SV_ERR_BAD_SHAPE, "%s: num_splits < 0", what);
-  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-    return fail(SV_ERR_BAD_SHAPE, "%s: scale must be finite", what);
+  if (!(scale > 0.0f) || scale == __builtin_inff())
+    return fail(SV_ERR_BAD_SHAPE, "%s: scale must be finite and positive", what);
   if (shape->num_seqs == 0) return ok();
   if (!q || !k_draft || !v_draft || !k_pool || !v_pool || !block_table || !ctx_lens || !idx ||
       !cnt || !out)
     return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
   const int splits = resolve_splits(shape, k_max, num_splits);
-  size_t ml_off;
-  const size_t need = attn_ws_layout(shape, splits, &ml_off);
+  size_t o_off, ml_off;
+  const size_t need = attn_ws_layout(shape, splits, &o_off, &ml_off);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
                 ws ? ws_bytes : static_cast<size_t>(0));
@@ -284,7 +288,8 @@ sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void
   p.cnt = cnt;
   p.out = out;
   p.lse = lse;
-  p.part_o = need ? reinterpret_cast<float*>(w) : nullptr;
+  p.tickets = need ? reinterpret_cast<uint32_t*>(w) : nullptr;
+  p.part_o = need ? reinterpret_cast<float*>(w + o_off) : nullptr;
   p.part_ml = need ? reinterpret_cast<float*>(w + ml_off) : nullptr;
   p.B = shape->num_seqs;
   p.Hq = shape->num_q_heads;
@@ -298,6 +303,7 @@ sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void
   p.k_max = k_max;
   p.S = splits;
   p.R = shape->num_draft * p.G;
+  p.fuse_merge = sv::attn_fuses_merge(splits, p.R, p.D) ? 1 : 0;
   p.scale_log2 = scale * 1.44269504088896340736f;
   return from_hip(sv::launch_attn(p, shape->dtype == SV_BF16, static_cast<hipStream_t>(stream)),
                   what);

@@ -5,54 +5,119 @@
 //
 // Work unit = (sequence b, KV head g). Its rows are the T x G (draft token, query
 // head of the group) pairs, padded to RP in {16, 32, 64, 128}; its keys are the
-// valid tokens of the selected blocks followed by the T draft tokens (draft t sees
-// drafts 0..t). The keys of a unit are cut into tiles of TT tokens (one tile never
-// spans two blocks); split s of S takes a contiguous range of context tiles, and
-// the last split also takes the draft tile.
+// valid tokens of the selected blocks plus the T draft tokens (draft t sees drafts
+// 0..t). Keys are cut into tiles of TT tokens (a tile never spans two blocks); split
+// s of S takes a contiguous range of context tiles, and one more workgroup per unit
+// takes the draft tile alone (with S == 1 the single split takes it first).
 //
-// Per workgroup: tiles stream HBM -> LDS with 16-byte LDS-DMA loads
-// (global_load_lds_dwordx4), double-buffered, so the next tile is in flight while
-// the current one is computed. LDS rows are XOR-swizzled in 16-byte chunks so the
-// MFMA operand reads (16 lanes, 16 different rows, same chunk) hit distinct banks.
-// Each wave owns RW rows and a subset of the tile's 32-token groups and computes
+// Prologue: the sequence's block-table row, the split's block indices and the
+// query fragments are requested together, so the chain before the first tile is
+// one dependent load (selected count -> indices).
+//
+// Data movement: tiles stream HBM -> LDS through 16-byte LDS-DMA loads
+// (global_load_lds_dwordx4) into a ring of NBUF buffers (two workgroups share a CU),
+// so the next tile is in flight while one is computed. The DMA is issued from inline
+// assembly and waited for with explicit vmcnt counts (every tile is exactly LPW
+// loads per lane, and no other vector load sits in the loop). LDS rows are
+// XOR-swizzled in 16-byte chunks so the MFMA operand reads (16 lanes, 16 rows, one
+// chunk) hit distinct banks.
+//
+// Compute, per wave (16 rows, a subset of a tile's 32-token groups):
 //   S^T = K Q^T      (MFMA, M = tokens, N = rows, K = head dim)
-//   online softmax in log2 units per row (rows live on lanes, so the running max,
-//   denominator and rescale factor are lane-local after a 4-lane reduction)
+//   online softmax in log2 units: the scale folds into one FMA per score, rows live
+//   on lanes, so max / denominator / rescale are lane-local after a 4-lane swap
+//   reduction, and the accumulators are rescaled only when some row max moved
 //   O^T += V^T P^T   (MFMA, M = head dim, N = rows, K = tokens)
-// The token order inside a 32-token group is permuted so that the S^T accumulator
-// a lane holds is exactly the P^T operand it must feed, and V^T (the pool keeps V
-// dim-major inside a block) gives the matching operand as one 16-byte LDS read.
-// bf16 uses v_mfma_f32_16x16x32_bf16, fp32 uses v_mfma_f32_16x16x4_f32; both
-// accumulate in fp32.
+// Token order inside a 32-token group is permuted so the S^T accumulator a lane
+// holds is exactly the P^T operand it feeds, and the pool's dim-major V blocks give
+// the matching V^T operand as one 16-byte LDS read. Full context tiles take a path
+// with no per-token masking. bf16 uses v_mfma_f32_16x16x32_bf16, fp32
+// v_mfma_f32_16x16x4_f32; accumulation is fp32.
 //
-// With S == 1 the workgroup normalises and writes the output; otherwise it writes
-// an unnormalised partial (O, running max, denominator) and merge_kernel combines
-// the S partials of a row:  O = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
+// Merge of the partials of a unit:  O = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
+//  - S == 1: the workgroup normalises and writes the output itself.
+//  - small partial volume: each workgroup writes its partial with device-scope
+//    (sc1, coherent across XCDs) stores, waits for them, and takes a ticket from a
+//    per-unit arrival counter; the last workgroup to arrive reads the partials back
+//    with device-scope 16-byte loads and writes the output, then clears the counter.
+//    No cache writeback fence is needed because every access to the partials is
+//    device-scope.
+//  - otherwise merge_kernel combines the partials in a second launch.
 #include "internal.h"
 
 namespace sv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-
-#define SV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+typedef unsigned int u32x4v __attribute__((__vector_size__(16)));
+typedef unsigned int u32x2v __attribute__((__vector_size__(8)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kBtStageMax = 1024;    // block-table rows up to this length are staged in LDS
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  // vmcnt in bits [3:0] and [15:14]; expcnt (bits [6:4]) and lgkmcnt (bits [11:8])
-  // left at their maximum so they do not wait.
+  // vmcnt in bits [3:0] and [15:14]; expcnt [6:4] and lgkmcnt [11:8] at maximum.
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Workgroup barrier that orders LDS accesses but leaves outstanding global loads
-// (the LDS-DMA prefetch) in flight.
+// Workgroup barrier that orders LDS accesses but leaves the LDS-DMA prefetch in
+// flight.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte LDS-DMA load per lane: lane i's 16 bytes at `src` land at LDS byte
+// address lds + 16*i (lds is wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+// Reductions over the 4 lanes l, l^16, l^32, l^48 (the lanes holding one row) with
+// the gfx950 cross-row lane swaps (VALU, no LDS round trip).
+__device__ __forceinline__ float max_over_row_lanes(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                  false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+__device__ __forceinline__ float sum_over_row_lanes(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, untyped); accesses past the
+// end return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// Device-scope (sc1) accesses: coherent across the XCDs' L2 caches without a cache
+// writeback, which is what lets the last split of a unit read its siblings'
+// partials.
+constexpr int kDeviceScope = 16;
+__device__ __forceinline__ void store_dev4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ f32x4 load_dev4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
+}
+__device__ __forceinline__ void store_dev2(__amdgpu_buffer_rsrc_t r, int off, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ float2 load_dev2(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kDeviceScope));
 }
 
 template <bool BF16_, int D_, int TT_, int RP_>
@@ -62,7 +127,7 @@ struct Cfg {
   static constexpr int TT = TT_;           // tokens per tile
   static constexpr int RP = RP_;           // padded rows
   static constexpr int ES = BF16 ? 2 : 4;  // element bytes
-  static constexpr int RW = RP < 32 ? RP : 32;   // rows per wave
+  static constexpr int RW = 16;                   // rows per wave (one MFMA N-tile)
   static constexpr int NRG = RP / RW;             // row groups
   static constexpr int NGRP = TT / 32;            // 32-token groups per tile
   static constexpr int NTG = NRG >= 4 ? 1 : NGRP; // waves sharing a row group
@@ -77,11 +142,23 @@ struct Cfg {
   static constexpr int TILE_CH = KCH + VCH;
   static constexpr int TILE_BYTES = TILE_CH * 16;
   static constexpr int LPW = TILE_CH / NT;        // LDS-DMA loads per lane per tile
-  static constexpr int NBUF = 2;
+  // Ring depth: two workgroups share a CU, so each keeps about 64 KB of tiles;
+  // vmcnt holds at most 63 outstanding loads.
+  static constexpr int NBUF_VM = 1 + 63 / LPW;
+  static constexpr int NBUF_LDS = 65536 / TILE_BYTES;
+  static constexpr int NBUF = NBUF_VM < NBUF_LDS ? (NBUF_VM < 4 ? NBUF_VM : 4)
+                                                 : (NBUF_LDS < 4 ? NBUF_LDS : 4);
   static constexpr int KFC = NCHK / 4;            // K chunks per lane (a quarter row)
+  static constexpr int VPM = BF16 ? 1 : 2;        // 16-byte V^T chunks per lane per md
   static constexpr int MERGE_BYTES = ((NTG - 1) * RP * D + 2 * NTG * RP) * 4;
-  static constexpr int LDS_BYTES =
+  static constexpr int RING_BYTES =
       NBUF * TILE_BYTES > MERGE_BYTES ? NBUF * TILE_BYTES : MERGE_BYTES;
+  static constexpr int DESC_OFF = RING_BYTES;                            // int2 per block
+  static constexpr int BT_OFF = DESC_OFF + kAttnMaxBlocksPerSplit * 8;   // staged table row
+  static constexpr int FLAG_OFF = BT_OFF + kBtStageMax * 4;
+  static constexpr int LDS_BYTES = FLAG_OFF + 16;
+  static constexpr int BT_PER = (kBtStageMax + NT - 1) / NT;
+  static_assert(NBUF >= 2, "need at least double buffering");
   static_assert(TILE_CH % NT == 0, "tile must split evenly over the lanes");
   static_assert(KCH % 64 == 0, "a wave load must not straddle K and V");
   static_assert((NBUF - 1) * LPW < 64, "vmcnt range");
@@ -96,30 +173,225 @@ __device__ __forceinline__ int swz_k(int r) {
   return NCH >= 16 ? mu : (mu >> 1);
 }
 
+// V^T rows (head dims) read together are 16 consecutive rows. For 128-byte rows the
+// XOR keeps both every 8-lane and every 16-lane phase of a 16-byte read on
+// distinct banks (row r and r+8 share parity, so they differ in the low bit).
 template <int NCH>
 __device__ __forceinline__ int swz_v(int r) {
-  return NCH == 16 ? (r & 15) : NCH == 8 ? ((r & 15) >> 1) : ((r & 15) >> 2);
+  return NCH == 16 ? (r & 15)
+       : NCH == 8  ? ((r & 7) ^ ((r >> 3) & 1))
+                   : ((r & 15) >> 2);
 }
 
-// Token (within a 32-token group) held by MFMA M-row m of M-tile mt. Chosen so
-// that lane l of the S^T result holds tokens 8*(l/16) .. 8*(l/16)+7.
+// Token (within a 32-token group) held by MFMA M-row m of M-tile mt, chosen so that
+// lane l of the S^T result holds tokens 8*(l/16) .. 8*(l/16)+7.
 __device__ __forceinline__ int tau(int mt, int m) { return 8 * (m >> 2) + 4 * mt + (m & 3); }
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) {
-  return __uint_as_float(static_cast<uint32_t>(x) << 16);
-}
 
 __device__ __forceinline__ uint4 lds_read16(const char* base, int chunk) {
   return *reinterpret_cast<const uint4*>(base + chunk * 16);
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT) void attn_kernel(AttnParams p) {
+__device__ __forceinline__ void wait_for_tile(int n_after) {
+  // n_after = DMA tiles issued after the one about to be used (0 .. NBUF-2).
+  if constexpr (C::NBUF >= 4) {
+    if (n_after >= 2) { wait_vmcnt<2 * C::LPW>(); return; }
+  }
+  if constexpr (C::NBUF >= 3) {
+    if (n_after >= 1) { wait_vmcnt<C::LPW>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// Running softmax state of one wave: O^T accumulators, row max (log2 units, scaled)
+// and the lane-partial denominators.
+template <class C>
+struct WaveState {
+  f32x4 o[C::NMD][C::NN];
+  float m[C::NN];
+  float l[C::NN];
+};
+
+// One 32-token group of one tile for one wave. MASKED: tokens >= nvalid (and, for
+// the draft tile, tokens after the row's own draft) are excluded. DRAFT: V is
+// token-major in LDS (the draft tile) instead of dim-major.
+template <class C, bool MASKED, bool DRAFT>
+__device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase,
+                                             const char* vbase, int grp, int nvalid,
+                                             const uint4 (&qf)[C::NN][C::KFC],
+                                             const int (&trow)[C::NN], float c, int l16, int g4) {
+  constexpr int ES = C::ES;
+  const int tok0 = grp * 32 + 8 * g4;
+  const int vc = (tok0 * ES) >> 4;
+  // Every LDS fragment of the group is requested up front so the reads overlap
+  // each other and the S^T MFMAs.
+  uint4 kf[2][C::KFC];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int r = grp * 32 + tau(mt, l16);
+#pragma unroll
+    for (int kc = 0; kc < C::KFC; ++kc)
+      kf[mt][kc] = lds_read16(kbase, r * C::NCHK + ((C::KFC * g4 + kc) ^ swz_k<C::NCHK>(r)));
+  }
+  uint4 vf[C::NMD][C::VPM];
+  if constexpr (!DRAFT) {
+#pragma unroll
+    for (int md = 0; md < C::NMD; ++md) {
+      const int r = md * 16 + l16;
+#pragma unroll
+      for (int e = 0; e < C::VPM; ++e)
+        vf[md][e] = lds_read16(vbase, r * C::NCHV + ((vc + e) ^ swz_v<C::NCHV>(r)));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- S^T = K Q^T
+  f32x4 sacc[2][C::NN];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < C::NN; ++nt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < C::KFC; ++kc) {
+        if constexpr (C::BF16) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[mt][kc]),
+                                                        __builtin_bit_cast(bf16x8_t, qf[nt][kc]),
+                                                        acc, 0, 0, 0);
+        } else {
+          const f32x4 ka = __builtin_bit_cast(f32x4, kf[mt][kc]);
+          const f32x4 qa = __builtin_bit_cast(f32x4, qf[nt][kc]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qa[e], acc, 0, 0, 0);
+        }
+      }
+      sacc[mt][nt] = acc;
+    }
+  }
+
+  // ---- online softmax; the lane holds tokens tok0 + 0..7 of row l16. Scores are
+  // raw dot products; c = scale * log2(e) > 0 commutes with the max.
+  float pv[C::NN][8];
+#pragma unroll
+  for (int nt = 0; nt < C::NN; ++nt) {
+    float s[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const float x = sacc[jj >> 2][nt][jj & 3];
+      if constexpr (MASKED) {
+        const int tok = tok0 + jj;
+        const bool vis = tok < nvalid && (!DRAFT || tok <= trow[nt]);
+        s[jj] = vis ? x : -__builtin_inff();
+      } else {
+        s[jj] = x;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    mx = max_over_row_lanes(mx);
+    const float mnew = fmaxf(st.m[nt], mx * c);
+    const float msafe = mnew == -__builtin_inff() ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(st.m[nt] - msafe);
+    float ls = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      pv[nt][jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jj], c, -msafe));
+      ls += pv[nt][jj];
+    }
+    st.l[nt] = st.l[nt] * alpha + ls;
+    st.m[nt] = mnew;
+    // Rescale the accumulators only if some row's max moved (exact skip).
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int md = 0; md < C::NMD; ++md) st.o[md][nt] *= alpha;
+    }
+  }
+
+  // ---- O^T += V^T P^T
+  if constexpr (!DRAFT) {
+    if constexpr (C::BF16) {
+      bf16x8_t pf[C::NN];
+#pragma unroll
+      for (int nt = 0; nt < C::NN; ++nt)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) pf[nt][jj] = static_cast<__bf16>(pv[nt][jj]);
+#pragma unroll
+      for (int md = 0; md < C::NMD; ++md)
+#pragma unroll
+        for (int nt = 0; nt < C::NN; ++nt)
+          st.o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, vf[md][0]), pf[nt], st.o[md][nt], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int md = 0; md < C::NMD; ++md) {
+        const f32x4 v0 = __builtin_bit_cast(f32x4, vf[md][0]);
+        const f32x4 v1 = __builtin_bit_cast(f32x4, vf[md][C::VPM - 1]);
+#pragma unroll
+        for (int nt = 0; nt < C::NN; ++nt) {
+          f32x4 acc = st.o[md][nt];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[e], pv[nt][e], acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[e], pv[nt][4 + e], acc, 0, 0, 0);
+          st.o[md][nt] = acc;
+        }
+      }
+    }
+  } else {
+    // Draft tile: V is token-major [TT][D] (K-style swizzle); gather the lane's 8
+    // tokens of one head dim element by element.
+    constexpr int EPC = 16 / ES;
+#pragma unroll
+    for (int md = 0; md < C::NMD; ++md) {
+      const int dim = md * 16 + l16;
+      const int ch = dim / EPC;
+      const int off = (dim % EPC) * ES;
+      float v[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int r = tok0 + jj;
+        const char* src = vbase + (r * C::NCHK + (ch ^ swz_k<C::NCHK>(r))) * 16 + off;
+        if constexpr (C::BF16)
+          v[jj] = __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(src))
+                                  << 16);
+        else
+          v[jj] = *reinterpret_cast<const float*>(src);
+      }
+#pragma unroll
+      for (int nt = 0; nt < C::NN; ++nt) {
+        if constexpr (C::BF16) {
+          bf16x8_t a, pf;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            a[jj] = static_cast<__bf16>(v[jj]);
+            pf[jj] = static_cast<__bf16>(pv[nt][jj]);
+          }
+          st.o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, st.o[md][nt], 0, 0, 0);
+        } else {
+          f32x4 acc = st.o[md][nt];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[jj], pv[nt][jj], acc, 0, 0, 0);
+          st.o[md][nt] = acc;
+        }
+      }
+    }
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT, C::BF16 ? 2 : 1) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  constexpr int ES = C::ES;
+  constexpr int D = C::D;
+  constexpr int TT = C::TT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave / C::NTG;
   const int tg = wave % C::NTG;
   const int l16 = lane & 15;
@@ -129,128 +401,178 @@ __global__ __launch_bounds__(C::NT) void attn_kernel(AttnParams p) {
   const int unit = blockIdx.y;
   const int b = unit / p.Hkv;
   const int g = unit - b * p.Hkv;
-  const int S = p.S;
+  const int S = p.S;                  // context splits
+  const int NP = S > 1 ? S + 1 : 1;   // partials per unit (+1: the draft-only split)
+  const bool draft_split = S > 1 && split == S;
+  const int tpb = p.bs / TT;
 
-  int ctx = p.ctx_lens[b];
+  // ---------------------------------------------------------------- prologue
+  // Requests that do not depend on the selected count go out first: the block-table
+  // row (staged in LDS when short enough) and the query fragments.
+  const int32_t* gbt = p.block_table + static_cast<int64_t>(b) * p.NB;
+  int* bt_lds = reinterpret_cast<int*>(smem + C::BT_OFF);
+  const bool bt_staged = p.NB <= kBtStageMax;
+  int btv[C::BT_PER];
+  if (bt_staged) {
+#pragma unroll
+    for (int u = 0; u < C::BT_PER; ++u) {
+      const int i = tid + u * C::NT;
+      btv[u] = i < p.NB ? gbt[i] : 0;
+    }
+  }
+
+  // Row r of this wave's N-tile nt: (draft t, head hl) = (row / G, row % G).
+  const int row0 = rg * C::RW;
+  uint4 qf[C::NN][C::KFC];
+  int trow[C::NN];
+  {
+    const char* qbase = static_cast<const char*>(p.q);
+#pragma unroll
+    for (int nt = 0; nt < C::NN; ++nt) {
+      const int row = row0 + nt * 16 + l16;
+      const int t = row / p.G;
+      trow[nt] = t;
+      const bool ok = row < p.R;
+      const int h = g * p.G + (row - t * p.G);
+      const char* src = qbase + ((static_cast<int64_t>(b) * p.T + t) * p.Hq + h) * D * ES;
+#pragma unroll
+      for (int kc = 0; kc < C::KFC; ++kc)
+        qf[nt][kc] = ok ? *reinterpret_cast<const uint4*>(src + (C::KFC * g4 + kc) * 16)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  // Scalar: context length and selected count -> this split's tile range.
+  const cint_ptr s_ctx = (cint_ptr)(p.ctx_lens);
+  const cint_ptr s_cnt = (cint_ptr)(p.cnt);
+  int ctx = s_ctx[b];
   if (ctx < 0) ctx = 0;
   int nb = (ctx + p.bs - 1) / p.bs;
   if (nb > p.NB) nb = p.NB;
-  int nsel = p.cnt[unit];
+  int nsel = s_cnt[unit];
   if (nsel > p.k_max) nsel = p.k_max;
   if (nsel < 0) nsel = 0;
-  const int tpb = p.bs / C::TT;
   const int nt_ctx = nsel * tpb;
   const int tps = (nt_ctx + S - 1) / S;
-  int t_begin = split * tps;
+  int t_begin = draft_split ? nt_ctx : split * tps;
   if (t_begin > nt_ctx) t_begin = nt_ctx;
-  int t_end = t_begin + tps;
+  int t_end = draft_split ? nt_ctx : t_begin + tps;
   if (t_end > nt_ctx) t_end = nt_ctx;
-  const int n_ctx_tiles = t_end - t_begin;
-  const bool has_draft = (split == S - 1);
-  const int ntiles = n_ctx_tiles + (has_draft ? 1 : 0);
+  // The draft tile: its own split when S > 1, else the single split's first tile.
+  const int has_draft = (S == 1 || draft_split) ? 1 : 0;
+  const int ntiles = (t_end - t_begin) + has_draft;
+  const int q0 = t_begin / tpb;
+  int nblk = t_end > t_begin ? (t_end - 1) / tpb - q0 + 1 : 0;
+  if (nblk > kAttnMaxBlocksPerSplit) nblk = kAttnMaxBlocksPerSplit;
 
-  const int32_t* sel_idx = p.idx + static_cast<int64_t>(unit) * p.k_max;
-  const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.NB;
+  // Block descriptors of this split: desc[q] = (physical block, valid tokens of the
+  // block), or (0, -1) for an index outside [0, nb) or a bad table entry.
+  int2* desc = reinterpret_cast<int2*>(smem + C::DESC_OFF);
+  const int32_t* gidx = p.idx + static_cast<int64_t>(unit) * p.k_max + q0;
+  int jv = -1;
+  if (tid < nblk) jv = gidx[tid];
+  if (bt_staged) {
+#pragma unroll
+    for (int u = 0; u < C::BT_PER; ++u) {
+      const int i = tid + u * C::NT;
+      if (i < p.NB) bt_lds[i] = btv[u];
+    }
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+  for (int i = tid; i < nblk; i += C::NT) {
+    const int j = i == tid ? jv : gidx[i];
+    const bool jok = j >= 0 && j < nb;
+    const int pb = bt_staged ? bt_lds[jok ? j : 0] : gbt[jok ? j : 0];
+    const bool ok = jok && pb >= 0 && pb < p.P;
+    desc[i] = ok ? make_int2(pb, ctx - j * p.bs) : make_int2(0, -1);
+  }
+  wait_vmcnt<0>();   // nothing but the DMA stream is outstanding from here on
+  lds_barrier();
+
   const char* kpool = static_cast<const char*>(p.k_pool);
   const char* vpool = static_cast<const char*>(p.v_pool);
-  constexpr int ES = C::ES;
-  constexpr int D = C::D;
-  constexpr int TT = C::TT;
+  const char* kdraft = static_cast<const char*>(p.k_draft) +
+                       (static_cast<int64_t>(b) * p.T * p.Hkv + g) * D * ES;
+  const char* vdraft = static_cast<const char*>(p.v_draft) +
+                       (static_cast<int64_t>(b) * p.T * p.Hkv + g) * D * ES;
+  const int64_t draft_row = static_cast<int64_t>(p.Hkv) * D * ES;   // bytes between drafts
+  const uint32_t smem_base =
+      static_cast<uint32_t>((uintptr_t)((__attribute__((address_space(3))) char*)(smem)));
 
-  // Context tile i of this split -> physical block, token offset, valid tokens.
-  auto tile_info = [&](int i, int& phys, int& tt0, int& nvalid) {
-    const int ti = t_begin + i;
-    const int j = sel_idx[ti / tpb];
-    tt0 = (ti - (ti / tpb) * tpb) * TT;
-    phys = 0;
-    nvalid = 0;
-    if (j >= 0 && j < nb) {
-      const int pb = bt[j];
-      if (pb >= 0 && pb < p.P) {
-        phys = pb;
-        int n = ctx - j * p.bs - tt0;
-        nvalid = n < 0 ? 0 : (n > TT ? TT : n);
-      }
-    }
+  // Tile i of this split: the draft tile first (if owned), then context tiles.
+  // Context tile -> physical block, token offset inside it, valid tokens (0 for a
+  // bad block index; such a tile still moves LPW loads from block 0 so the vmcnt
+  // accounting stays uniform, and is not computed).
+  auto ctx_tile = [&](int i, int& phys, int& tt0, int& nvalid) {
+    const int ti = t_begin + i - has_draft;
+    const int q = ti / tpb;
+    tt0 = (ti - q * tpb) * TT;
+    int qi = q - q0;
+    if (qi >= kAttnMaxBlocksPerSplit) qi = kAttnMaxBlocksPerSplit - 1;   // never for valid S
+    const int2 d = desc[qi];
+    phys = __builtin_amdgcn_readfirstlane(d.x);
+    const int avail = __builtin_amdgcn_readfirstlane(d.y);
+    const int n = avail - tt0;
+    nvalid = avail < 0 ? 0 : (n < 0 ? 0 : (n > TT ? TT : n));
   };
 
-  // Asynchronous HBM -> LDS copy of context tile i into buffer buf (LPW loads per
-  // lane). Tiles with no valid token still issue their loads (from block 0) so that
-  // every context tile accounts for exactly LPW outstanding loads.
-  auto issue_tile = [&](int i, int buf) {
-    int phys, tt0, nv;
-    tile_info(i, phys, tt0, nv);
-    const int64_t blk = static_cast<int64_t>(phys) * p.Hkv + g;
-    const char* kb = kpool + (blk * p.bs + tt0) * D * ES;
-    const char* vb = vpool + blk * D * p.bs * ES + tt0 * ES;
-    char* lbase = smem + buf * C::TILE_BYTES;
+  // Per-lane source offsets of the LPW context-tile loads: the same for every tile
+  // (only the block base changes), so they are computed once.
+  int dma_off[C::LPW];
 #pragma unroll
-    for (int u = 0; u < C::LPW; ++u) {
-      const int cbase = (u * C::NWAVE + wave) * 64;
-      const int ch = cbase + lane;
-      const char* src;
-      if (cbase < C::KCH) {
-        const int r = ch / C::NCHK;
-        const int c = (ch % C::NCHK) ^ swz_k<C::NCHK>(r);
-        src = kb + r * (D * ES) + c * 16;
-      } else {
-        const int q = ch - C::KCH;
-        const int r = q / C::NCHV;
-        const int c = (q % C::NCHV) ^ swz_v<C::NCHV>(r);
-        src = vb + static_cast<int64_t>(r) * p.bs * ES + c * 16;
-      }
-      __builtin_amdgcn_global_load_lds(src, SV_LDS(lbase + cbase * 16), 16, 0, 0);
-    }
-  };
-
-  // Synchronous load of the draft tile (T <= 16 tokens, natural [t][d] layout)
-  // into buffer buf, transposing V; slots past T are zero.
-  auto load_draft = [&](int buf) {
-    char* lbase = smem + buf * C::TILE_BYTES;
-    const char* kd = static_cast<const char*>(p.k_draft);
-    const char* vd = static_cast<const char*>(p.v_draft);
-    for (int ch = tid; ch < C::KCH; ch += C::NT) {
+  for (int u = 0; u < C::LPW; ++u) {
+    const int cbase = (u * C::NWAVE + wave) * 64;
+    const int ch = cbase + lane;
+    if (cbase < C::KCH) {
       const int r = ch / C::NCHK;
-      const int c = ch % C::NCHK;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < p.T)
-        v = *reinterpret_cast<const uint4*>(
-            kd + ((static_cast<int64_t>(b) * p.T + r) * p.Hkv + g) * D * ES + c * 16);
-      *reinterpret_cast<uint4*>(lbase + (r * C::NCHK + (c ^ swz_k<C::NCHK>(r))) * 16) = v;
+      dma_off[u] = r * (D * ES) + ((ch % C::NCHK) ^ swz_k<C::NCHK>(r)) * 16;
+    } else {
+      const int q = ch - C::KCH;
+      const int r = q / C::NCHV;
+      dma_off[u] = r * p.bs * ES + ((q % C::NCHV) ^ swz_v<C::NCHV>(r)) * 16;
     }
-    char* vbase = lbase + C::KCH * 16;
-    constexpr int EPC = 16 / ES;    // elements per chunk
-    for (int ch = tid; ch < C::VCH; ch += C::NT) {
-      const int r = ch / C::NCHV;   // head dim
-      const int c = ch % C::NCHV;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
+  }
+
+  auto issue = [&](int i, int buf) {
+    const uint32_t lbase = smem_base + buf * C::TILE_BYTES;
+    if (has_draft && i == 0) {
+      // Draft tile: K and V both token-major [TT][D]; rows >= T re-read draft 0
+      // (finite data, masked out of the softmax).
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const int t = c * EPC + e;
-        if (t < p.T) {
-          const char* src = vd + (((static_cast<int64_t>(b) * p.T + t) * p.Hkv + g) * D + r) * ES;
-          if constexpr (ES == 2) {
-            const uint32_t x = *reinterpret_cast<const uint16_t*>(src);
-            w[e >> 1] |= x << (16 * (e & 1));
-          } else {
-            w[e] = *reinterpret_cast<const uint32_t*>(src);
-          }
-        }
+      for (int u = 0; u < C::LPW; ++u) {
+        const int cbase = (u * C::NWAVE + wave) * 64;
+        const int ch = cbase + lane;
+        const int q = cbase < C::KCH ? ch : ch - C::KCH;
+        const int r = q / C::NCHK;
+        const int cc = (q % C::NCHK) ^ swz_k<C::NCHK>(r);
+        const char* base = cbase < C::KCH ? kdraft : vdraft;
+        dma16(base + (r < p.T ? r : 0) * draft_row + cc * 16, lbase + cbase * 16);
       }
-      *reinterpret_cast<uint4*>(vbase + (r * C::NCHV + (c ^ swz_v<C::NCHV>(r))) * 16) =
-          make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      int phys, tt0, nv;
+      ctx_tile(i, phys, tt0, nv);
+      const int64_t blk = static_cast<int64_t>(phys) * p.Hkv + g;
+      const char* kb = kpool + (blk * p.bs + tt0) * D * ES;
+      const char* vb = vpool + blk * D * p.bs * ES + tt0 * ES;
+#pragma unroll
+      for (int u = 0; u < C::LPW; ++u) {
+        const int cbase = (u * C::NWAVE + wave) * 64;
+        dma16((cbase < C::KCH ? kb : vb) + dma_off[u], lbase + cbase * 16);
+      }
     }
   };
 
-  // Zero V^T columns of tokens >= nvalid in buffer buf (partly filled last block).
+  // Zero V^T columns of tokens >= nvalid in buffer buf (partly filled last block):
+  // the pool holds arbitrary bits there and P = 0 must not meet a NaN.
   auto zero_tail = [&](int buf, int nvalid) {
     char* vbase = smem + buf * C::TILE_BYTES + C::KCH * 16;
     const int ntail = TT - nvalid;
     for (int e = tid; e < D * ntail; e += C::NT) {
       const int r = e / ntail;
       const int t = nvalid + (e - r * ntail);
-      const int c = (t * ES) >> 4;
-      char* dst = vbase + (r * C::NCHV + (c ^ swz_v<C::NCHV>(r))) * 16 + ((t * ES) & 15);
+      const int cc = (t * ES) >> 4;
+      char* dst = vbase + (r * C::NCHV + (cc ^ swz_v<C::NCHV>(r))) * 16 + ((t * ES) & 15);
       if constexpr (ES == 2)
         *reinterpret_cast<uint16_t*>(dst) = 0;
       else
@@ -258,178 +580,61 @@ __global__ __launch_bounds__(C::NT) void attn_kernel(AttnParams p) {
     }
   };
 
-  // ---------------------------------------------------------------- Q fragments
-  // Row r of this wave's N-tile nt: (draft t, head hl) = (row / G, row % G).
-  const int row0 = rg * C::RW;
-  const char* qbase = static_cast<const char*>(p.q);
-  uint4 qf[C::NN][C::KFC];
-  int trow[C::NN];
+  WaveState<C> st;
 #pragma unroll
   for (int nt = 0; nt < C::NN; ++nt) {
-    const int row = row0 + nt * 16 + l16;
-    const int t = row / p.G;
-    trow[nt] = t;
-    const bool ok = row < p.R;
-    const int h = g * p.G + (row - t * p.G);
-    const char* src = qbase + ((static_cast<int64_t>(b) * p.T + t) * p.Hq + h) * D * ES;
+    st.m[nt] = -__builtin_inff();
+    st.l[nt] = 0.0f;
 #pragma unroll
-    for (int kc = 0; kc < C::KFC; ++kc)
-      qf[nt][kc] = ok ? *reinterpret_cast<const uint4*>(src + (C::KFC * g4 + kc) * 16)
-                      : make_uint4(0u, 0u, 0u, 0u);
+    for (int md = 0; md < C::NMD; ++md) st.o[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  f32x4 oacc[C::NMD][C::NN];
-  float mrow[C::NN], lrow[C::NN];
-#pragma unroll
-  for (int nt = 0; nt < C::NN; ++nt) {
-    mrow[nt] = -__builtin_inff();
-    lrow[nt] = 0.0f;
-#pragma unroll
-    for (int md = 0; md < C::NMD; ++md) oacc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  const float c = p.scale_log2;
 
   // ---------------------------------------------------------------- tile loop
-  auto issue_any = [&](int i) {
-    const int buf = i % C::NBUF;
-    if (i < n_ctx_tiles) issue_tile(i, buf); else load_draft(buf);
-  };
 #pragma unroll
   for (int i = 0; i < C::NBUF - 1; ++i)
-    if (i < ntiles) issue_any(i);
+    if (i < ntiles) issue(i, i);
 
   for (int it = 0; it < ntiles; ++it) {
+    int last_issued = it + C::NBUF - 2;
+    if (last_issued > ntiles - 1) last_issued = ntiles - 1;
+    wait_for_tile<C>(last_issued - it);
+    lds_barrier();                      // tile `it` landed for all waves; it-1 done
     const int nxt = it + C::NBUF - 1;
-    if (nxt < ntiles) issue_any(nxt);
-    int n_after = (n_ctx_tiles - 1 < nxt ? n_ctx_tiles - 1 : nxt) - it;
-    if (n_after > 0) wait_vmcnt<C::LPW>(); else wait_vmcnt<0>();
-    lds_barrier();
+    if (nxt < ntiles) issue(nxt, nxt % C::NBUF);
 
-    const bool is_draft = it >= n_ctx_tiles;
-    int nvalid;
-    if (is_draft) {
-      nvalid = p.T;
-    } else {
-      int phys, tt0;
-      tile_info(it, phys, tt0, nvalid);
-      if (nvalid > 0 && nvalid < TT) {
-        zero_tail(it % C::NBUF, nvalid);
-        lds_barrier();
-      }
-    }
-    const char* kbase = smem + (it % C::NBUF) * C::TILE_BYTES;
+    const int buf = it % C::NBUF;
+    const char* kbase = smem + buf * C::TILE_BYTES;
     const char* vbase = kbase + C::KCH * 16;
-
-    for (int grp = tg; grp < C::NGRP; grp += C::NTG) {
-      if (grp * 32 >= nvalid) break;
-      // ---- S^T = K Q^T for the 32 tokens of this group
-      f32x4 sacc[2][C::NN];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int r = grp * 32 + tau(mt, l16);
-        uint4 kf[C::KFC];
-#pragma unroll
-        for (int kc = 0; kc < C::KFC; ++kc)
-          kf[kc] = lds_read16(kbase, r * C::NCHK + ((C::KFC * g4 + kc) ^ swz_k<C::NCHK>(r)));
-#pragma unroll
-        for (int nt = 0; nt < C::NN; ++nt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kc = 0; kc < C::KFC; ++kc) {
-            if constexpr (C::BF16) {
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, kf[kc]), __builtin_bit_cast(bf16x8_t, qf[nt][kc]),
-                  acc, 0, 0, 0);
-            } else {
-              const f32x4 ka = __builtin_bit_cast(f32x4, kf[kc]);
-              const f32x4 qa = __builtin_bit_cast(f32x4, qf[nt][kc]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qa[e], acc, 0, 0, 0);
-            }
-          }
-          sacc[mt][nt] = acc;
-        }
+    if (has_draft && it == 0) {
+#pragma unroll 1
+      for (int grp = tg; grp < C::NGRP; grp += C::NTG) {
+        if (grp * 32 >= p.T) break;
+        attend_group<C, true, true>(st, kbase, vbase, grp, p.T, qf, trow, c, l16, g4);
       }
-      // ---- online softmax (log2 units); lane holds tokens tok0 + 0..7 of row l16
-      const int tok0 = grp * 32 + 8 * g4;
-      float pv[C::NN][8];
-#pragma unroll
-      for (int nt = 0; nt < C::NN; ++nt) {
-        float s[8];
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int tok = tok0 + jj;
-          const bool vis = tok < nvalid && (!is_draft || tok <= trow[nt]);
-          const float x = sacc[jj >> 2][nt][jj & 3] * p.scale_log2;
-          s[jj] = vis ? x : -__builtin_inff();
-          mx = fmaxf(mx, s[jj]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(mrow[nt], mx);
-        const float msafe = mnew == -__builtin_inff() ? 0.0f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(mrow[nt] - msafe);
-        float ls = 0.0f;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          pv[nt][jj] = __builtin_amdgcn_exp2f(s[jj] - msafe);
-          ls += pv[nt][jj];
-        }
-        lrow[nt] = lrow[nt] * alpha + ls;
-        mrow[nt] = mnew;
-#pragma unroll
-        for (int md = 0; md < C::NMD; ++md) oacc[md][nt] *= alpha;
-      }
-      // ---- O^T += V^T P^T
-      if constexpr (C::BF16) {
-        bf16x8_t pf[C::NN];
-#pragma unroll
-        for (int nt = 0; nt < C::NN; ++nt)
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) pf[nt][jj] = static_cast<__bf16>(pv[nt][jj]);
-        const int vc = (tok0 * ES) >> 4;
-#pragma unroll
-        for (int md = 0; md < C::NMD; ++md) {
-          const int r = md * 16 + l16;
-          const uint4 vf = lds_read16(vbase, r * C::NCHV + (vc ^ swz_v<C::NCHV>(r)));
-#pragma unroll
-          for (int nt = 0; nt < C::NN; ++nt)
-            oacc[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, vf), pf[nt], oacc[md][nt], 0, 0, 0);
-        }
-      } else {
-        const int vc = (tok0 * ES) >> 4;
-#pragma unroll
-        for (int md = 0; md < C::NMD; ++md) {
-          const int r = md * 16 + l16;
-          const f32x4 v0 = __builtin_bit_cast(
-              f32x4, lds_read16(vbase, r * C::NCHV + (vc ^ swz_v<C::NCHV>(r))));
-          const f32x4 v1 = __builtin_bit_cast(
-              f32x4, lds_read16(vbase, r * C::NCHV + ((vc + 1) ^ swz_v<C::NCHV>(r))));
-#pragma unroll
-          for (int nt = 0; nt < C::NN; ++nt) {
-            f32x4 acc = oacc[md][nt];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[e], pv[nt][e], acc, 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[e], pv[nt][4 + e], acc, 0, 0, 0);
-            oacc[md][nt] = acc;
-          }
-        }
+      continue;
+    }
+    int phys, tt0, nvalid;
+    ctx_tile(it, phys, tt0, nvalid);
+    if (nvalid == TT) {
+#pragma unroll 1
+      for (int grp = tg; grp < C::NGRP; grp += C::NTG)
+        attend_group<C, false, false>(st, kbase, vbase, grp, TT, qf, trow, c, l16, g4);
+    } else if (nvalid > 0) {
+      zero_tail(buf, nvalid);
+      lds_barrier();
+#pragma unroll 1
+      for (int grp = tg; grp < C::NGRP; grp += C::NTG) {
+        if (grp * 32 >= nvalid) break;
+        attend_group<C, true, false>(st, kbase, vbase, grp, nvalid, qf, trow, c, l16, g4);
       }
     }
-    lds_barrier();
   }
+  lds_barrier();   // every wave is done with the tile buffers
 
   // ---------------------------------------------------------------- finish
 #pragma unroll
-  for (int nt = 0; nt < C::NN; ++nt) {
-    lrow[nt] += __shfl_xor(lrow[nt], 16, 64);
-    lrow[nt] += __shfl_xor(lrow[nt], 32, 64);
-  }
+  for (int nt = 0; nt < C::NN; ++nt) st.l[nt] = sum_over_row_lanes(st.l[nt]);
 
   if constexpr (C::NTG > 1) {
     // Combine the waves that share a row group: stats[tg][row][2], then the O^T
@@ -440,59 +645,61 @@ __global__ __launch_bounds__(C::NT) void attn_kernel(AttnParams p) {
     for (int nt = 0; nt < C::NN; ++nt) {
       const int row = row0 + nt * 16 + l16;
       if (g4 == 0) {
-        stats[(tg * C::RP + row) * 2 + 0] = mrow[nt];
-        stats[(tg * C::RP + row) * 2 + 1] = lrow[nt];
+        stats[(tg * C::RP + row) * 2 + 0] = st.m[nt];
+        stats[(tg * C::RP + row) * 2 + 1] = st.l[nt];
       }
       if (tg > 0) {
 #pragma unroll
         for (int md = 0; md < C::NMD; ++md)
           *reinterpret_cast<f32x4*>(olds + (static_cast<int64_t>(tg - 1) * C::RP + row) * D +
-                                    md * 16 + 4 * g4) = oacc[md][nt];
+                                    md * 16 + 4 * g4) = st.o[md][nt];
       }
     }
     lds_barrier();
-    if (tg > 0) return;
+    if (tg == 0) {
 #pragma unroll
-    for (int nt = 0; nt < C::NN; ++nt) {
-      const int row = row0 + nt * 16 + l16;
-      float mmax = -__builtin_inff();
+      for (int nt = 0; nt < C::NN; ++nt) {
+        const int row = row0 + nt * 16 + l16;
+        float mmax = -__builtin_inff();
 #pragma unroll
-      for (int w = 0; w < C::NTG; ++w) mmax = fmaxf(mmax, stats[(w * C::RP + row) * 2]);
-      const float msafe = mmax == -__builtin_inff() ? 0.0f : mmax;
-      const float a0 = __builtin_amdgcn_exp2f(mrow[nt] - msafe);
-      float l = lrow[nt] * a0;
+        for (int w = 0; w < C::NTG; ++w) mmax = fmaxf(mmax, stats[(w * C::RP + row) * 2]);
+        const float msafe = mmax == -__builtin_inff() ? 0.0f : mmax;
+        const float a0 = __builtin_amdgcn_exp2f(st.m[nt] - msafe);
+        float l = st.l[nt] * a0;
 #pragma unroll
-      for (int md = 0; md < C::NMD; ++md) oacc[md][nt] *= a0;
+        for (int md = 0; md < C::NMD; ++md) st.o[md][nt] *= a0;
 #pragma unroll
-      for (int w = 1; w < C::NTG; ++w) {
-        const float aw = __builtin_amdgcn_exp2f(stats[(w * C::RP + row) * 2] - msafe);
-        l += stats[(w * C::RP + row) * 2 + 1] * aw;
+        for (int w = 1; w < C::NTG; ++w) {
+          const float aw = __builtin_amdgcn_exp2f(stats[(w * C::RP + row) * 2] - msafe);
+          l += stats[(w * C::RP + row) * 2 + 1] * aw;
 #pragma unroll
-        for (int md = 0; md < C::NMD; ++md)
-          oacc[md][nt] += aw * *reinterpret_cast<const f32x4*>(
-                                   olds + (static_cast<int64_t>(w - 1) * C::RP + row) * D +
-                                   md * 16 + 4 * g4);
+          for (int md = 0; md < C::NMD; ++md)
+            st.o[md][nt] += aw * *reinterpret_cast<const f32x4*>(
+                                     olds + (static_cast<int64_t>(w - 1) * C::RP + row) * D +
+                                     md * 16 + 4 * g4);
+        }
+        st.m[nt] = mmax;
+        st.l[nt] = l;
       }
-      mrow[nt] = mmax;
-      lrow[nt] = l;
     }
   }
 
   // ---------------------------------------------------------------- write
+  const bool writer = tg == 0;
+  if (S == 1) {
+    if (!writer) return;
 #pragma unroll
-  for (int nt = 0; nt < C::NN; ++nt) {
-    const int row = row0 + nt * 16 + l16;
-    if (row >= p.R) continue;
-    const int t = row / p.G;
-    const int h = g * p.G + (row - t * p.G);
-    if (S == 1) {
-      const float inv = 1.0f / lrow[nt];
+    for (int nt = 0; nt < C::NN; ++nt) {
+      const int row = row0 + nt * 16 + l16;
+      if (row >= p.R) continue;
+      const int t = row / p.G;
+      const int h = g * p.G + (row - t * p.G);
+      const float inv = 1.0f / st.l[nt];
       const int64_t o = ((static_cast<int64_t>(b) * p.T + t) * p.Hq + h) * D;
 #pragma unroll
       for (int md = 0; md < C::NMD; ++md) {
-        const f32x4 v = oacc[md][nt] * inv;
+        const f32x4 v = st.o[md][nt] * inv;
         if constexpr (C::BF16) {
-          typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
           bf16x4_t w;
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = static_cast<__bf16>(v[e]);
@@ -503,41 +710,148 @@ __global__ __launch_bounds__(C::NT) void attn_kernel(AttnParams p) {
       }
       if (p.lse && g4 == 0)
         p.lse[(static_cast<int64_t>(b) * p.T + t) * p.Hq + h] =
-            (mrow[nt] + __builtin_log2f(lrow[nt])) * kLn2;
-    } else {
-      const int64_t prow = (static_cast<int64_t>(unit) * S + split) * p.R + row;
+            (st.m[nt] + __builtin_log2f(st.l[nt])) * kLn2;
+    }
+    return;
+  }
+
+  // Partial of this split: O (unnormalised), running max (log2 units), denominator,
+  // written with device-scope stores.
+  const int part_bytes = NP * p.R * D * 4;
+  const __amdgpu_buffer_rsrc_t po =
+      make_rsrc(p.part_o + static_cast<int64_t>(unit) * NP * p.R * D, part_bytes);
+  const __amdgpu_buffer_rsrc_t pml =
+      make_rsrc(p.part_ml + static_cast<int64_t>(unit) * NP * p.R * 2, NP * p.R * 8);
+  if (writer) {
+#pragma unroll
+    for (int nt = 0; nt < C::NN; ++nt) {
+      const int row = row0 + nt * 16 + l16;
+      if (row >= p.R) continue;
+      const int prow = split * p.R + row;
 #pragma unroll
       for (int md = 0; md < C::NMD; ++md)
-        *reinterpret_cast<f32x4*>(p.part_o + prow * D + md * 16 + 4 * g4) = oacc[md][nt];
-      if (g4 == 0) {
-        p.part_ml[prow * 2 + 0] = mrow[nt];
-        p.part_ml[prow * 2 + 1] = lrow[nt];
-      }
+        store_dev4(po, (prow * D + md * 16 + 4 * g4) * 4, st.o[md][nt]);
+      if (g4 == 0) store_dev2(pml, prow * 8, make_float2(st.m[nt], st.l[nt]));
+    }
+  }
+  if (!p.fuse_merge) return;
+
+  // Arrival: every partial store of this workgroup has completed before the ticket
+  // is taken.
+  wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  lds_barrier();
+  int* flag = reinterpret_cast<int*>(smem + C::FLAG_OFF);
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(p.tickets + unit, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    *flag = (prev == static_cast<unsigned>(NP - 1)) ? 1 : 0;
+  }
+  lds_barrier();
+  if (*flag == 0) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (tid == 0)
+    __hip_atomic_store(p.tickets + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // Last workgroup of the unit. Phase 1: per row, the weight of every partial,
+  // w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s', into LDS (and the row's LSE).
+  float* wts = reinterpret_cast<float*>(smem);     // [R][NP]
+  for (int row = tid; row < p.R; row += C::NT) {
+    float mmax = -__builtin_inff();
+    for (int s2 = 0; s2 < NP; ++s2) mmax = fmaxf(mmax, load_dev2(pml, (s2 * p.R + row) * 8).x);
+    const float msafe = mmax == -__builtin_inff() ? 0.0f : mmax;
+    float l = 0.0f;
+    for (int s2 = 0; s2 < NP; ++s2) {
+      const float2 ml = load_dev2(pml, (s2 * p.R + row) * 8);
+      const float w = __builtin_amdgcn_exp2f(ml.x - msafe);
+      wts[row * NP + s2] = w;
+      l += w * ml.y;
+    }
+    const float inv = 1.0f / l;
+    for (int s2 = 0; s2 < NP; ++s2) wts[row * NP + s2] *= inv;
+    if (p.lse) {
+      const int t = row / p.G;
+      const int h = g * p.G + (row - t * p.G);
+      p.lse[(static_cast<int64_t>(b) * p.T + t) * p.Hq + h] = (mmax + __builtin_log2f(l)) * kLn2;
+    }
+  }
+  lds_barrier();
+  // Phase 2: out = sum_s w_s O_s, 4 head dims per thread, all loads of an item in
+  // flight together.
+  for (int i4 = tid; i4 * 4 < p.R * D; i4 += C::NT) {
+    const int row = (i4 * 4) / D;
+    const int dim = i4 * 4 - row * D;
+    f32x4 os[kAttnFusedMaxPartials];
+#pragma unroll
+    for (int s2 = 0; s2 < kAttnFusedMaxPartials; ++s2)
+      if (s2 < NP) os[s2] = load_dev4(po, ((s2 * p.R + row) * D + dim) * 4);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < kAttnFusedMaxPartials; ++s2)
+      if (s2 < NP) o += wts[row * NP + s2] * os[s2];
+    const int t = row / p.G;
+    const int h = g * p.G + (row - t * p.G);
+    const int64_t off = ((static_cast<int64_t>(b) * p.T + t) * p.Hq + h) * D + dim;
+    if constexpr (C::BF16) {
+      bf16x4_t w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = static_cast<__bf16>(o[e]);
+      *reinterpret_cast<bf16x4_t*>(static_cast<char*>(p.out) + off * 2) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = o;
     }
   }
 }
 
-// Combine the S partials of every (unit, row): one thread per 4 head dims.
+// Combine the S partials of every (unit, row) in one pass over the splits, eight
+// splits per batch of loads (a running max rescales the accumulated sum). One
+// thread per 4 head dims.
+constexpr int kMergeThreads = 64;
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   const int unit = blockIdx.y;
-  const int i4 = blockIdx.x * 256 + threadIdx.x;
+  const int i4 = blockIdx.x * kMergeThreads + threadIdx.x;
   const int D = p.D;
   if (i4 * 4 >= p.R * D) return;
   const int row = (i4 * 4) / D;
   const int dim = i4 * 4 - row * D;
-  const int S = p.S;
+  const int S = p.S + 1;   // context splits plus the draft split
   const int64_t base = static_cast<int64_t>(unit) * S * p.R + row;
-  float mmax = -__builtin_inff();
-  for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, p.part_ml[(base + static_cast<int64_t>(s) * p.R) * 2]);
-  const float msafe = mmax == -__builtin_inff() ? 0.0f : mmax;
-  float l = 0.0f;
+  constexpr int BATCH = 8;
+  float mrun = -__builtin_inff(), l = 0.0f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const int64_t pr = base + static_cast<int64_t>(s) * p.R;
-    const float a = __builtin_amdgcn_exp2f(p.part_ml[pr * 2] - msafe);
-    l += a * p.part_ml[pr * 2 + 1];
-    o += a * *reinterpret_cast<const f32x4*>(p.part_o + pr * D + dim);
+  for (int s0 = 0; s0 < S; s0 += BATCH) {
+    float m[BATCH], ls[BATCH];
+    f32x4 os[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      if (s0 + k < S) {
+        const int64_t pr = base + static_cast<int64_t>(s0 + k) * p.R;
+        const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + pr * 2);
+        m[k] = ml.x;
+        ls[k] = ml.y;
+        os[k] = *reinterpret_cast<const f32x4*>(p.part_o + pr * D + dim);
+      } else {
+        m[k] = -__builtin_inff();
+        ls[k] = 0.0f;
+        os[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float mb = mrun;
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) mb = fmaxf(mb, m[k]);
+    const float msafe = mb == -__builtin_inff() ? 0.0f : mb;
+    const float a = __builtin_amdgcn_exp2f(mrun - msafe);
+    l *= a;
+    o *= a;
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const float w = __builtin_amdgcn_exp2f(m[k] - msafe);
+      l += w * ls[k];
+      o += w * os[k];
+    }
+    mrun = mb;
   }
   const int b = unit / p.Hkv;
   const int g = unit - b * p.Hkv;
@@ -546,7 +860,6 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
   const int64_t off = ((static_cast<int64_t>(b) * p.T + t) * p.Hq + h) * D + dim;
   const f32x4 v = o * (1.0f / l);
   if constexpr (BF16) {
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
     bf16x4_t w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = static_cast<__bf16>(v[e]);
@@ -555,12 +868,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = v;
   }
   if (p.lse && dim == 0)
-    p.lse[(static_cast<int64_t>(b) * p.T + t) * p.Hq + h] = (mmax + __builtin_log2f(l)) * kLn2;
+    p.lse[(static_cast<int64_t>(b) * p.T + t) * p.Hq + h] = (mrun + __builtin_log2f(l)) * kLn2;
 }
 
 template <class C>
 hipError_t launch_cfg(const AttnParams& p, hipStream_t stream) {
-  dim3 grid(p.S, p.B * p.Hkv);
+  dim3 grid(p.S > 1 ? p.S + 1 : 1, p.B * p.Hkv);
   hipLaunchKernelGGL(attn_kernel<C>, grid, dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
@@ -577,24 +890,32 @@ hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
 
 template <bool BF16>
 hipError_t launch_dtype(const AttnParams& p, hipStream_t stream) {
-  const int tt = attn_tile_tokens(p.bs);
-  if (p.D == 128) {
-    return tt == 64 ? launch_rows<BF16, 128, 64>(p, stream) : launch_rows<BF16, 128, 32>(p, stream);
+  if constexpr (BF16) {
+    const bool t64 = attn_tile_tokens(p.bs, true) == 64;
+    if (p.D == 128)
+      return t64 ? launch_rows<true, 128, 64>(p, stream) : launch_rows<true, 128, 32>(p, stream);
+    return t64 ? launch_rows<true, 64, 64>(p, stream) : launch_rows<true, 64, 32>(p, stream);
+  } else {
+    return p.D == 128 ? launch_rows<false, 128, 32>(p, stream) : launch_rows<false, 64, 32>(p, stream);
   }
-  return tt == 64 ? launch_rows<BF16, 64, 64>(p, stream) : launch_rows<BF16, 64, 32>(p, stream);
 }
 
 }  // namespace
 
+bool attn_fuses_merge(int splits, int rows, int head_dim) {
+  return splits > 1 && splits + 1 <= kAttnFusedMaxPartials &&
+         static_cast<int64_t>(splits + 1) * rows * head_dim * 4 <= kAttnFusedMergeBytes;
+}
+
 hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
   hipError_t e = bf16 ? launch_dtype<true>(p, stream) : launch_dtype<false>(p, stream);
-  if (e != hipSuccess || p.S == 1) return e;
-  dim3 grid((p.R * p.D / 4 + 255) / 256, p.B * p.Hkv);
+  if (e != hipSuccess || p.S == 1 || p.fuse_merge) return e;
+  dim3 grid((p.R * p.D / 4 + kMergeThreads - 1) / kMergeThreads, p.B * p.Hkv);
   if (bf16)
-    hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(kMergeThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(merge_kernel<false>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<false>, grid, dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -29,7 +29,6 @@ struct SelectParams {
   int32_t* idx;
   int32_t* cnt;
   float* scores;        // [B, Hkv, NB] (user buffer or workspace)
-  uint32_t* tickets;    // [B * Hkv] arrival counters, zero between calls
   int32_t scores_requested;   // nonzero: write scores even where every block is kept
   int32_t B, Hq, Hkv, G, D, T, bs, NB, P, k_max;
   int32_t dense_ctx, min_blocks, frac_per_mille, keep_first, keep_last;
@@ -47,10 +46,14 @@ struct AttnParams {
   const int32_t* cnt;
   void* out;
   float* lse;
-  float* part_o;        // [units, S, R, D] unnormalised partial outputs
-  float* part_ml;       // [units, S, R, 2]  (running max in log2 units, denominator)
-  int32_t B, Hq, Hkv, G, D, T, bs, NB, P, k_max, S, R;
-  float scale_log2;     // softmax scale * log2(e)
+  float* part_o;        // [units, S+1, R, D] unnormalised partial outputs
+  float* part_ml;       // [units, S+1, R, 2]  (running max in log2 units, denominator)
+  uint32_t* tickets;    // [units] arrival counters of the fused merge, zero between calls
+  int32_t fuse_merge;   // nonzero: the last split of a unit merges (no merge kernel)
+  int32_t B, Hq, Hkv, G, D, T, bs, NB, P, k_max;
+  int32_t S;            // context splits (a draft-only split is added when S > 1)
+  int32_t R;
+  float scale_log2;     // softmax scale * log2(e), > 0
 };
 
 struct ReuseParams {
@@ -68,10 +71,15 @@ struct ReuseParams {
 hipError_t launch_block_repr(const ReprParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream);
+// Whether the attention kernel merges its splits itself (small partial volume).
+bool attn_fuses_merge(int splits, int rows, int head_dim);
 hipError_t launch_reuse(const ReuseParams& p, hipStream_t stream);
 
-// Tokens per attention tile for a block size (a tile never spans two blocks).
-inline int attn_tile_tokens(int block_size) { return block_size < 64 ? block_size : 64; }
+// Tokens per attention tile (a tile never spans two blocks): 64 for bf16 blocks of
+// 64 or more tokens, else 32.
+inline int attn_tile_tokens(int block_size, bool bf16) {
+  return (bf16 && block_size >= 64) ? 64 : 32;
+}
 
 // Padded row count of the (draft token x GQA head) tile.
 inline int attn_padded_rows(int rows) {
@@ -79,6 +87,13 @@ inline int attn_padded_rows(int rows) {
 }
 
 constexpr int kSelectChunk = 128;     // blocks scored by one select workgroup
+// Most selected blocks one attention split stages descriptors for (the split count
+// is raised so that no split covers more).
+constexpr int kAttnMaxBlocksPerSplit = 1024;
+// Largest per-unit partial volume (S x rows x head_dim x 4 bytes) merged by the
+// last attention workgroup of the unit instead of a separate merge launch.
+constexpr int64_t kAttnFusedMergeBytes = 160 * 1024;
+constexpr int kAttnFusedMaxPartials = 17;
 constexpr int kSelectThreads = 256;
 
 }  // namespace sv

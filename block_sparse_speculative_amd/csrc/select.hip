@@ -4,13 +4,16 @@
 // Verification", section "Core technique 1"; sciencestack page of arXiv 2512.21911,
 // Figure 1 caption).
 //
-// One launch. Grid = (ceil(NB / 128) chunks, Hkv, B); workgroup (c, g, b) scores
-// blocks [128c, 128c+128) of sequence b for KV head g, streaming the float32
-// representatives through the block table (one 16-byte load per lane, D/4 lanes
-// per block, shuffle reduction in a fixed order). The last workgroup to finish for
-// (b, g) -- found with an arrival counter -- runs the budget and an LDS radix
-// select on order-preserving 32-bit keys, then compacts the chosen indices in
-// ascending order with block-wide scans. The counter is reset by that workgroup.
+// Two launches.
+//  score_kernel  grid = (ceil(NB / 128) chunks, Hkv, B): workgroup (c, g, b) scores
+//                blocks [128c, 128c+128) of sequence b for KV head g, streaming the
+//                float32 representatives through the block table (one 16-byte load
+//                per lane, D/4 lanes per block, shuffle reduction in a fixed order).
+//                Sequences whose budget keeps every block are skipped unless the
+//                caller asked for the scores.
+//  topk_kernel   grid = (Hkv, B): budget, then an LDS radix select on
+//                order-preserving 32-bit keys and an ascending compaction of the
+//                chosen indices with block-wide scans.
 #include "internal.h"
 
 namespace sv {
@@ -66,12 +69,7 @@ __device__ __forceinline__ int budget_blocks_dev(const SelectParams& p, int ctx,
 }
 
 template <typename E, int D>
-__global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
-  extern __shared__ uint32_t keys[];           // [NB] (top-k phase only)
-  __shared__ int hist[256];
-  __shared__ int scan_scratch[NWAVE];
-  __shared__ int bcast[4];
-
+__global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -106,19 +104,22 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
         qs[e] += v;
       }
     }
+    // All block-table loads first, then all representative loads: no branch
+    // between them, so every load of the workgroup is in flight at once.
     float4 r[PASSES];
-    int jj[PASSES];
+    int jj[PASSES], ph[PASSES];
 #pragma unroll
     for (int u = 0; u < PASSES; ++u) {
       const int j = j0 + (u * NWAVE + wave) * BPW + sub;
       jj[u] = j;
-      r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < nb) {
-        const int phys = bt[j];
-        if (phys >= 0 && phys < p.P)
-          r[u] = *reinterpret_cast<const float4*>(
-              p.repr_pool + (static_cast<int64_t>(phys) * p.Hkv + g) * D + 4 * li);
-      }
+      ph[u] = bt[j < nb ? j : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < PASSES; ++u) {
+      const bool ok = jj[u] < nb && ph[u] >= 0 && ph[u] < p.P;
+      r[u] = *reinterpret_cast<const float4*>(
+          p.repr_pool + (static_cast<int64_t>(ok ? ph[u] : 0) * p.Hkv + g) * D + 4 * li);
+      if (!ok) r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < PASSES; ++u) {
@@ -132,22 +133,28 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
     }
   }
 
-  // ------------------------------------------------------------ arrival
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(p.tickets + unit, 1u);
-    bcast[0] = (prev == gridDim.x - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!bcast[0]) return;
-  __threadfence();
+}
+
+__global__ __launch_bounds__(NT) void topk_kernel(SelectParams p) {
+  extern __shared__ uint32_t keys[];           // [NB]
+  __shared__ int hist[256];
+  __shared__ int scan_scratch[NWAVE];
+  __shared__ int bcast[4];
+
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int unit = b * p.Hkv + g;
+  int ctx = p.ctx_lens[b];
+  if (ctx < 0) ctx = 0;
+  int nb = (ctx + p.bs - 1) / p.bs;
+  if (nb > p.NB) nb = p.NB;
+  const float* sc = p.scores + static_cast<int64_t>(unit) * p.NB;
 
   // ------------------------------------------------------------ budget + top-k
   int k = budget_blocks_dev(p, ctx, nb);
   if (k > p.k_max) k = p.k_max;
   int32_t* out = p.idx + static_cast<int64_t>(unit) * p.k_max;
-  if (tid == 0) p.tickets[unit] = 0u;
   if (k >= nb) {
     if (tid == 0) p.cnt[unit] = nb;
     for (int pos = tid; pos < p.k_max; pos += NT) out[pos] = pos < nb ? pos : -1;
@@ -162,10 +169,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
   const int E_PER = (nb + NT - 1) / NT;       // contiguous keys owned by each thread
   const int my_lo = tid * E_PER;
   const int my_hi = my_lo + E_PER < nb ? my_lo + E_PER : nb;
-  for (int j = my_lo; j < my_hi; ++j) {
+  for (int j = tid; j < nb; j += NT) {
     const bool forced = (j == f0) || (j == f1);
-    const float s = __hip_atomic_load(sc + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    keys[j] = forced ? 0u : score_key(s);
+    keys[j] = forced ? 0u : score_key(sc[j]);
   }
   __syncthreads();
 
@@ -241,18 +247,21 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams p) {
 hipError_t launch_select(const SelectParams& p, bool bf16, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
   dim3 grid((p.NB + kSelectChunk - 1) / kSelectChunk, p.Hkv, p.B);
-  const size_t lds = static_cast<size_t>(p.NB) * sizeof(uint32_t);
   if (bf16) {
     if (p.D == 128)
-      hipLaunchKernelGGL((select_kernel<uint16_t, 128>), grid, dim3(NT), lds, stream, p);
+      hipLaunchKernelGGL((score_kernel<uint16_t, 128>), grid, dim3(NT), 0, stream, p);
     else
-      hipLaunchKernelGGL((select_kernel<uint16_t, 64>), grid, dim3(NT), lds, stream, p);
+      hipLaunchKernelGGL((score_kernel<uint16_t, 64>), grid, dim3(NT), 0, stream, p);
   } else {
     if (p.D == 128)
-      hipLaunchKernelGGL((select_kernel<float, 128>), grid, dim3(NT), lds, stream, p);
+      hipLaunchKernelGGL((score_kernel<float, 128>), grid, dim3(NT), 0, stream, p);
     else
-      hipLaunchKernelGGL((select_kernel<float, 64>), grid, dim3(NT), lds, stream, p);
+      hipLaunchKernelGGL((score_kernel<float, 64>), grid, dim3(NT), 0, stream, p);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = static_cast<size_t>(p.NB) * sizeof(uint32_t);
+  hipLaunchKernelGGL(topk_kernel, dim3(p.Hkv, p.B), dim3(NT), lds, stream, p);
   return hipGetLastError();
 }
 

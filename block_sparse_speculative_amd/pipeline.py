@@ -58,14 +58,14 @@ def fill_pool(shape: L.Shape, pool: Pool, k_ctx, v_ctx, ctx_lens, block_table, c
 
 
 class Workspaces:
-    """Caller-owned workspaces: the selection one starts zeroed (its arrival
-    counters are left zeroed by every completed call)."""
+    """Caller-owned workspaces of the selection and attention entry points."""
 
     def __init__(self, shape: L.Shape, k_max: int, num_splits: int = 0, device="cuda"):
-        self.sel = torch.zeros(max(L.select_workspace_bytes(shape, k_max), 1), dtype=torch.uint8,
+        self.sel = torch.empty(max(L.select_workspace_bytes(shape, k_max), 1), dtype=torch.uint8,
                                device=device)
         n = L.attn_workspace_bytes(shape, k_max, num_splits)
-        self.attn = torch.empty(n, dtype=torch.uint8, device=device) if n else None
+        # zero-filled once: the attention workspace starts with arrival counters
+        self.attn = torch.zeros(n, dtype=torch.uint8, device=device) if n else None
         self.num_splits = num_splits
 
 

@@ -35,7 +35,7 @@ class Instance:
     def __init__(self, w: synth.Workload, seed: int = 0, device="cuda", num_layers: Optional[int] = None,
                  ctx_lens: Optional[List[int]] = None, paged: Optional[bool] = None,
                  num_splits: int = 0, with_lse: bool = True, nan_pool: bool = False,
-                 k_max: Optional[int] = None, append_chunk: int = 0):
+                 k_max: Optional[int] = None, append_chunk: int = 0, progress=None):
         if paged is not None:
             w = w.with_(paged=paged)
         self.w = w
@@ -71,6 +71,8 @@ class Instance:
                 lse=torch.empty((B, T, Hq), dtype=torch.float32, device=self.device)
                 if with_lse else None))
             del x
+            if progress is not None:
+                progress(l + 1, n_layers)
 
     def logical(self, layer: int):
         """Regenerate layer `layer`'s logical (unpaged) inputs on the device."""
@@ -100,30 +102,49 @@ class Instance:
 
     # --------------------------------------------------------------- accounting
     def selected_tokens(self) -> int:
-        """Context tokens attended in one pass, summed over layers, sequences and
-        KV heads (host arithmetic on the budget and context lengths)."""
-        bs = self.w.block_size
-        total = 0
-        for c in self.ctx_lens:
-            nb = -(-c // bs)
-            k = L.budget_blocks(self.budget, c, bs)
-            if k >= nb:
-                toks = c
-            else:
-                # every sparse selection holds the last (possibly partial) block
-                toks = k * bs - (nb * bs - c if self.budget.keep_last else 0)
-            total += toks
-        return total * self.w.num_kv_heads * len(self.layers)
+        return selected_tokens(self.w, self.ctx_lens, len(self.layers))
 
     def algorithmic_bytes(self) -> int:
-        """Bytes of selected K/V plus representatives scored in one pass."""
-        esz = 4 if self.w.dtype == "fp32" else 2
-        kv = self.selected_tokens() * self.w.head_dim * 2 * esz
-        bs = self.w.block_size
-        select_layers = sum(1 for ly in self.layers if not ly.reuse)
-        reps = sum(-(-c // bs) for c in self.ctx_lens) * self.w.num_kv_heads * self.w.head_dim * 4
-        return kv + reps * select_layers
+        return algorithmic_bytes(self.w, self.ctx_lens, len(self.layers))
 
     def units(self) -> int:
         """Verified (draft token, query head) rows per pass, summed over layers."""
         return self.w.num_seqs * self.w.num_draft * self.w.num_q_heads * len(self.layers)
+
+
+def _select_layers(w: synth.Workload, num_layers: int) -> int:
+    return sum(1 for l in range(num_layers) if not (w.reuse_odd_layers and l % 2 == 1))
+
+
+def selected_tokens(w: synth.Workload, ctx_lens, num_layers: int) -> int:
+    """Context tokens attended in one pass, summed over layers, sequences and KV heads
+    (host arithmetic on the budget and the context lengths)."""
+    budget = L.make_budget(*w.budget)
+    bs = w.block_size
+    total = 0
+    for c in ctx_lens:
+        nb = -(-c // bs)
+        k = L.budget_blocks(budget, c, bs)
+        if k >= nb:
+            toks = c
+        else:
+            # a sparse selection always holds the last (possibly partial) block
+            toks = k * bs - (nb * bs - c if budget.keep_last else 0)
+        total += toks
+    return total * w.num_kv_heads * num_layers
+
+
+def algorithmic_bytes(w: synth.Workload, ctx_lens, num_layers: int) -> int:
+    """Bytes of selected K/V read plus representatives scored in one pass; sequences
+    whose budget keeps every block are not scored."""
+    esz = 4 if w.dtype == "fp32" else 2
+    kv = selected_tokens(w, ctx_lens, num_layers) * w.head_dim * 2 * esz
+    budget = L.make_budget(*w.budget)
+    bs = w.block_size
+    scored_blocks = 0
+    for c in ctx_lens:
+        nb = -(-c // bs)
+        if L.budget_blocks(budget, c, bs) < nb:
+            scored_blocks += nb
+    reps = scored_blocks * w.num_kv_heads * w.head_dim * 4
+    return kv + reps * _select_layers(w, num_layers)

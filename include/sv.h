@@ -142,9 +142,9 @@ size_t sv_select_workspace_bytes(const sv_shape* shape, int32_t k_max);
  *   cnt        [B, Hkv]        int32 out: number of selected blocks (= k)
  *   scores     [B, Hkv, NB]    float32 out, optional (NULL): the block scores
  * k_max must be >= k for every sequence (use sv_budget_blocks); a larger k is
- * clamped to k_max. `ws` must hold sv_select_workspace_bytes() bytes, must be
- * zero-filled before its first use, and is left zero-filled by every call that
- * completes; do not share it with other entry points or with concurrent calls. */
+ * clamped to k_max. `ws` must hold sv_select_workspace_bytes() bytes (scratch for
+ * the scores when `scores` is NULL); its contents need no initialisation. Two
+ * kernels are enqueued (scoring, then budget + top-k). */
 sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const void* q,
                            const float* repr_pool, const int32_t* block_table,
                            const int32_t* ctx_lens, int32_t k_max, int32_t* idx,
@@ -152,7 +152,8 @@ sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const
                            void* stream);
 
 /* Number of KV splits sv_sparse_verify_attn uses: `num_splits` if > 0 (clamped to
- * the work available), else the library's choice for this shape. */
+ * the work available), else the library's choice for this shape. With more than one
+ * split, one extra workgroup per (sequence, KV head) handles the draft tokens. */
 int32_t sv_attn_num_splits(const sv_shape* shape, int32_t k_max, int32_t num_splits);
 
 /* Bytes of workspace sv_sparse_verify_attn needs (0 when one split is used). */
@@ -174,7 +175,10 @@ size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num
  *   out [B, T, Hq, D] dtype; lse [B, T, Hq] float32 or NULL
  * num_splits: 0 = library choice, else the number of KV splits (see
  * sv_attn_num_splits). `ws` must hold sv_attn_workspace_bytes() bytes (may be
- * NULL when that is 0); its contents need no initialisation. */
+ * NULL when that is 0). Its first B*Hkv*4 bytes are per-unit arrival counters that
+ * must be zero before the first call; every call that completes leaves them zero
+ * (zero-fill the workspace once at allocation; do not share it between calls that
+ * may run concurrently). scale must be finite and > 0. */
 sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,
                                 const void* v_draft, const void* k_pool, const void* v_pool,
                                 const int32_t* block_table, const int32_t* ctx_lens,

@@ -105,6 +105,8 @@ def test_attention_rejects_workspace_null_args_and_kmax():
     assert _attn(shape, k_max=0) == 2
     assert _attn(shape, k_max=2000) == 2
     assert _attn(shape, scale=float("nan")) == 2
+    assert _attn(shape, scale=0.0) == 2
+    assert _attn(shape, scale=-0.5) == 2
     assert _attn(shape, splits=-3) == 2
 
 

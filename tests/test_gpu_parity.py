@@ -254,3 +254,34 @@ def test_full_stack64k_sampled_layers_and_units():
     run_and_check(inst, units=[(0, 0), (3, 7), (2, 4)], layers=[0, 1, 30, 31], check_reps=False)
     del inst
     _free()
+
+
+def test_graph_replays_match_eager():
+    # The bench replays a captured pass; every replay must equal the eager pass.
+    _gpu()
+    w = W["stack64k"].with_(num_seqs=2, num_q_heads=8, num_kv_heads=2, ctx=(8192, 7000))
+    inst = Instance(w, seed=17, num_layers=4)
+    inst.step()
+    torch.cuda.synchronize()
+    eager = [(ly.idx.clone(), ly.cnt.clone(), ly.out.clone(), ly.lse.clone()) for ly in inst.layers]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        inst.step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        inst.step()
+    for rep in range(4):
+        for ly in inst.layers:           # clobber outputs so a stale value cannot pass
+            ly.idx.fill_(-5)
+            ly.out.fill_(float("nan"))
+            ly.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for ly, (i, c, o, s) in zip(inst.layers, eager):
+            assert torch.equal(ly.idx, i) and torch.equal(ly.cnt, c)
+            assert torch.equal(ly.out, o) and torch.equal(ly.lse, s)
+        inst.step()                     # eager work between replays
+        torch.cuda.synchronize()
