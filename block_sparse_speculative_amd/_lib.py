@@ -63,6 +63,10 @@ _SIG = [
     ("sv_attn_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(Shape), _I, _I]),
     ("sv_sparse_verify_attn", _I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                                    ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("sv_select_and_attend_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(Shape), _I, _I]),
+    ("sv_select_and_attend", _I, [ctypes.POINTER(Shape), ctypes.POINTER(Budget), _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _I, ctypes.c_float, _I, _P, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P]),
     ("sv_reuse_indices", _I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P]),
 ]
 EXPORTS = tuple(name for name, _, _ in _SIG)
@@ -214,6 +218,41 @@ def sparse_verify_attn(shape: Shape, q, k_draft, v_draft, k_pool, v_pool, block_
         ctypes.byref(shape), _ptr(q), _ptr(k_draft), _ptr(v_draft), _ptr(k_pool), _ptr(v_pool),
         _ptr(block_table), _ptr(ctx_lens), _ptr(idx), _ptr(cnt), int(k_max), float(scale),
         int(num_splits), _ptr(out), _ptr(lse), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream()))
+
+
+def select_and_attend_workspace_bytes(shape: Shape, k_max: int, num_splits: int = 0) -> int:
+    return lib().sv_select_and_attend_workspace_bytes(ctypes.byref(shape), int(k_max),
+                                                      int(num_splits))
+
+
+def select_and_attend(shape: Shape, budget: Budget, q, repr_pool, k_draft, v_draft, k_pool, v_pool,
+                      block_table, ctx_lens, k_max: int, scale: float, idx, cnt, out, lse=None,
+                      ws=None, num_splits: int = 0):
+    """sv_select_and_attend: selection and attention of one layer; writes idx / cnt."""
+    B, Hq, Hkv, D, T = (shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim,
+                        shape.num_draft)
+    e = _elem(shape)
+    P, bs = shape.num_phys_blocks, shape.block_size
+    _dev(q, "q", e, (B, T, Hq, D))
+    _dev(repr_pool, "repr_pool", torch.float32, (P, Hkv, D))
+    _dev(k_draft, "k_draft", e, (B, T, Hkv, D))
+    _dev(v_draft, "v_draft", e, (B, T, Hkv, D))
+    _dev(k_pool, "k_pool", e, (P, Hkv, bs, D))
+    _dev(v_pool, "v_pool", e, (P, Hkv, D, bs))
+    _dev(block_table, "block_table", torch.int32, (B, shape.max_blocks_per_seq))
+    _dev(ctx_lens, "ctx_lens", torch.int32, (B,))
+    _dev(idx, "idx", torch.int32, (B, Hkv, k_max))
+    _dev(cnt, "cnt", torch.int32, (B, Hkv))
+    _dev(out, "out", e, (B, T, Hq, D))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, T, Hq))
+    if ws is not None:
+        _dev(ws, "ws")
+    _check(lib().sv_select_and_attend(
+        ctypes.byref(shape), ctypes.byref(budget), _ptr(q), _ptr(repr_pool), _ptr(k_draft),
+        _ptr(v_draft), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(ctx_lens), int(k_max),
+        float(scale), int(num_splits), _ptr(idx), _ptr(cnt), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()))
 
 

@@ -94,14 +94,22 @@ sv_status check_kmax(const sv_shape* s, int32_t k_max, const char* what) {
   return SV_OK;
 }
 
+// Split count. Library choice: as many splits as keep every workgroup of the launch
+// resident at once (384 of the 512 slots when two workgroups share a CU, 256 when
+// each needs a CU: 128 padded rows or fp32), but no fewer than about four tiles per
+// split, so the per-workgroup prologue and the merge stay small next to the stream.
 int resolve_splits(const sv_shape* s, int32_t k_max, int32_t num_splits) {
   const int tt = sv::attn_tile_tokens(s->block_size, s->dtype == SV_BF16);
   const int64_t ctx_tiles = static_cast<int64_t>(k_max) * (s->block_size / tt);
   int64_t want = num_splits;
   if (want <= 0) {
     const int64_t units = static_cast<int64_t>(s->num_seqs) * s->num_kv_heads;
-    const int64_t target_wgs = 512;   // two attention workgroups per CU
-    want = units > 0 ? (target_wgs + units - 1) / units : 1;
+    const int64_t rows = static_cast<int64_t>(s->num_draft) * (s->num_q_heads / s->num_kv_heads);
+    const bool one_per_cu = rows > 64 || s->dtype != SV_BF16;
+    const int64_t target_wgs = one_per_cu ? sv::kAttnCUs : sv::kAttnCUs * 3 / 2;
+    want = units > 0 ? target_wgs / units - 1 : 1;
+    const int64_t by_tiles = (ctx_tiles + 3) / 4;
+    if (want > by_tiles) want = by_tiles;
   }
   if (want > ctx_tiles) want = ctx_tiles;
   // A split may straddle one block boundary at each end: keep it within the
@@ -118,8 +126,11 @@ size_t select_ws_layout(const sv_shape* s, size_t* scores_off) {
   return align_up(units * s->max_blocks_per_seq * sizeof(float));
 }
 
-// Attention workspace: [arrival counters: units x u32][partial O][partial (m, l)].
+// Attention workspace: [partial O][partial (m, l)].
 size_t attn_ws_layout(const sv_shape* s, int splits, size_t* o_off, size_t* ml_off) {
+  size_t o_dummy, ml_dummy;
+  if (!o_off) o_off = &o_dummy;
+  if (!ml_off) ml_off = &ml_dummy;
   if (splits <= 1) {
     *o_off = *ml_off = 0;
     return 0;
@@ -127,9 +138,86 @@ size_t attn_ws_layout(const sv_shape* s, int splits, size_t* o_off, size_t* ml_o
   const size_t rows = static_cast<size_t>(s->num_draft) * (s->num_q_heads / s->num_kv_heads);
   const size_t units = static_cast<size_t>(s->num_seqs) * s->num_kv_heads;
   const size_t parts = static_cast<size_t>(splits) + 1;   // + the draft-only split
-  *o_off = align_up(units * sizeof(uint32_t));
-  *ml_off = *o_off + align_up(units * parts * rows * s->head_dim * sizeof(float));
+  *o_off = 0;
+  *ml_off = align_up(units * parts * rows * s->head_dim * sizeof(float));
   return *ml_off + align_up(units * parts * rows * 2 * sizeof(float));
+}
+
+
+sv::SelectParams select_params(const sv_shape* shape, const sv_budget* budget, const void* q,
+                               const float* repr_pool, const int32_t* block_table,
+                               const int32_t* ctx_lens, int32_t k_max, int32_t* idx,
+                               int32_t* cnt) {
+  sv::SelectParams p{};
+  p.q = q;
+  p.repr_pool = repr_pool;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.idx = idx;
+  p.cnt = cnt;
+  p.B = shape->num_seqs;
+  p.Hq = shape->num_q_heads;
+  p.Hkv = shape->num_kv_heads;
+  p.G = shape->num_q_heads / shape->num_kv_heads;
+  p.D = shape->head_dim;
+  p.T = shape->num_draft;
+  p.bs = shape->block_size;
+  p.NB = shape->max_blocks_per_seq;
+  p.P = shape->num_phys_blocks;
+  p.k_max = k_max;
+  p.dense_ctx = budget->dense_ctx_tokens;
+  p.min_blocks = budget->min_blocks;
+  p.frac_per_mille = budget->frac_per_mille;
+  p.keep_first = budget->keep_first;
+  p.keep_last = budget->keep_last;
+  p.xcd_group = sv::xcd_groupable(p.B * p.Hkv) ? 1 : 0;
+  return p;
+}
+
+// Attention parameters with the workspace carved as attn_ws_layout says (ws may
+// be NULL when ws_need is 0); idx / cnt / scores are set by the caller.
+sv::AttnParams attn_params(const sv_shape* shape, const void* q, const void* k_draft,
+                           const void* v_draft, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const int32_t* ctx_lens, int32_t k_max,
+                           float scale, int splits, void* out, float* lse, void* ws,
+                           size_t ws_need) {
+  size_t o_off, ml_off;
+  attn_ws_layout(shape, splits, &o_off, &ml_off);
+  char* w = static_cast<char*>(ws);
+  sv::AttnParams p{};
+  p.q = q;
+  p.k_draft = k_draft;
+  p.v_draft = v_draft;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.out = out;
+  p.lse = lse;
+  p.part_o = ws_need ? reinterpret_cast<float*>(w + o_off) : nullptr;
+  p.part_ml = ws_need ? reinterpret_cast<float*>(w + ml_off) : nullptr;
+  p.B = shape->num_seqs;
+  p.Hq = shape->num_q_heads;
+  p.Hkv = shape->num_kv_heads;
+  p.G = shape->num_q_heads / shape->num_kv_heads;
+  p.D = shape->head_dim;
+  p.T = shape->num_draft;
+  p.bs = shape->block_size;
+  p.NB = shape->max_blocks_per_seq;
+  p.P = shape->num_phys_blocks;
+  p.k_max = k_max;
+  p.S = splits;
+  p.R = shape->num_draft * p.G;
+  p.xcd_group = sv::xcd_groupable(p.B * p.Hkv) ? 1 : 0;
+  p.scale_log2 = scale * 1.44269504088896340736f;
+  return p;
+}
+
+// Workspace of sv_select_and_attend: [attention partials][scores].
+size_t fused_ws_layout(const sv_shape* s, int splits, size_t* scores_off) {
+  *scores_off = align_up(attn_ws_layout(s, splits, nullptr, nullptr));
+  size_t sc_off;
+  return *scores_off + select_ws_layout(s, &sc_off);
 }
 
 }  // namespace
@@ -212,30 +300,10 @@ sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const
     return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
                 ws ? ws_bytes : static_cast<size_t>(0));
   char* w = static_cast<char*>(ws);
-  sv::SelectParams p{};
-  p.q = q;
-  p.repr_pool = repr_pool;
-  p.block_table = block_table;
-  p.ctx_lens = ctx_lens;
-  p.idx = idx;
-  p.cnt = cnt;
+  sv::SelectParams p = select_params(shape, budget, q, repr_pool, block_table, ctx_lens, k_max,
+                                     idx, cnt);
   p.scores = scores ? scores : reinterpret_cast<float*>(w + scores_off);
   p.scores_requested = scores != nullptr;
-  p.B = shape->num_seqs;
-  p.Hq = shape->num_q_heads;
-  p.Hkv = shape->num_kv_heads;
-  p.G = shape->num_q_heads / shape->num_kv_heads;
-  p.D = shape->head_dim;
-  p.T = shape->num_draft;
-  p.bs = shape->block_size;
-  p.NB = shape->max_blocks_per_seq;
-  p.P = shape->num_phys_blocks;
-  p.k_max = k_max;
-  p.dense_ctx = budget->dense_ctx_tokens;
-  p.min_blocks = budget->min_blocks;
-  p.frac_per_mille = budget->frac_per_mille;
-  p.keep_first = budget->keep_first;
-  p.keep_last = budget->keep_last;
   return from_hip(sv::launch_select(p, shape->dtype == SV_BF16, static_cast<hipStream_t>(stream)),
                   what);
 }
@@ -270,43 +338,80 @@ sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void
       !cnt || !out)
     return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
   const int splits = resolve_splits(shape, k_max, num_splits);
-  size_t o_off, ml_off;
-  const size_t need = attn_ws_layout(shape, splits, &o_off, &ml_off);
+  const size_t need = attn_ws_layout(shape, splits, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
                 ws ? ws_bytes : static_cast<size_t>(0));
-  char* w = static_cast<char*>(ws);
-  sv::AttnParams p{};
-  p.q = q;
-  p.k_draft = k_draft;
-  p.v_draft = v_draft;
-  p.k_pool = k_pool;
-  p.v_pool = v_pool;
-  p.block_table = block_table;
-  p.ctx_lens = ctx_lens;
+  sv::AttnParams p = attn_params(shape, q, k_draft, v_draft, k_pool, v_pool, block_table,
+                                 ctx_lens, k_max, scale, splits, out, lse, ws, need);
   p.idx = idx;
   p.cnt = cnt;
-  p.out = out;
-  p.lse = lse;
-  p.tickets = need ? reinterpret_cast<uint32_t*>(w) : nullptr;
-  p.part_o = need ? reinterpret_cast<float*>(w + o_off) : nullptr;
-  p.part_ml = need ? reinterpret_cast<float*>(w + ml_off) : nullptr;
-  p.B = shape->num_seqs;
-  p.Hq = shape->num_q_heads;
-  p.Hkv = shape->num_kv_heads;
-  p.G = shape->num_q_heads / shape->num_kv_heads;
-  p.D = shape->head_dim;
-  p.T = shape->num_draft;
-  p.bs = shape->block_size;
-  p.NB = shape->max_blocks_per_seq;
-  p.P = shape->num_phys_blocks;
-  p.k_max = k_max;
-  p.S = splits;
-  p.R = shape->num_draft * p.G;
-  p.fuse_merge = sv::attn_fuses_merge(splits, p.R, p.D) ? 1 : 0;
-  p.scale_log2 = scale * 1.44269504088896340736f;
   return from_hip(sv::launch_attn(p, shape->dtype == SV_BF16, static_cast<hipStream_t>(stream)),
                   what);
+}
+
+size_t sv_select_and_attend_workspace_bytes(const sv_shape* shape, int32_t k_max,
+                                            int32_t num_splits) {
+  if (check_shape(shape, "sv_select_and_attend_workspace_bytes") != SV_OK) return 0;
+  if (check_kmax(shape, k_max, "sv_select_and_attend_workspace_bytes") != SV_OK) return 0;
+  size_t scores_off;
+  return fused_ws_layout(shape, resolve_splits(shape, k_max, num_splits), &scores_off);
+}
+
+sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
+                               const float* repr_pool, const void* k_draft, const void* v_draft,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* ctx_lens,
+                               int32_t k_max, float scale, int32_t num_splits, int32_t* idx,
+                               int32_t* cnt, void* out, float* lse, void* ws, size_t ws_bytes,
+                               void* stream) {
+  const char* what = "sv_select_and_attend";
+  if (sv_status st = check_shape(shape, what)) return st;
+  if (sv_status st = check_budget(budget, what)) return st;
+  if (sv_status st = check_kmax(shape, k_max, what)) return st;
+  if (num_splits < 0) return fail(SV_ERR_BAD_SHAPE, "%s: num_splits < 0", what);
+  if (!(scale > 0.0f) || scale == __builtin_inff())
+    return fail(SV_ERR_BAD_SHAPE, "%s: scale must be finite and positive", what);
+  if (shape->num_seqs == 0) return ok();
+  if (!q || !repr_pool || !k_draft || !v_draft || !k_pool || !v_pool || !block_table ||
+      !ctx_lens || !idx || !cnt || !out)
+    return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  const int splits = resolve_splits(shape, k_max, num_splits);
+  size_t scores_off;
+  const size_t need = fused_ws_layout(shape, splits, &scores_off);
+  if (!ws || ws_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  const bool bf16 = shape->dtype == SV_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(w + scores_off);
+  sv::SelectParams sp = select_params(shape, budget, q, repr_pool, block_table, ctx_lens, k_max,
+                                      idx, cnt);
+  sp.scores = scores;
+  sp.scores_requested = 0;
+  const size_t attn_need = attn_ws_layout(shape, splits, nullptr, nullptr);
+  sv::AttnParams ap = attn_params(shape, q, k_draft, v_draft, k_pool, v_pool, block_table,
+                                  ctx_lens, k_max, scale, splits, out, lse, ws, attn_need);
+  ap.idx = idx;
+  ap.cnt = cnt;
+  hipError_t e = sv::launch_score(sp, bf16, st);
+  if (e != hipSuccess) return from_hip(e, what);
+  if (shape->max_blocks_per_seq <= sv::kWaveTopkMaxBlocks) {
+    // Budget + top-k run inside the attention workgroups.
+    ap.scores = scores;
+    ap.idx_out = idx;
+    ap.cnt_out = cnt;
+    ap.dense_ctx = budget->dense_ctx_tokens;
+    ap.min_blocks = budget->min_blocks;
+    ap.frac_per_mille = budget->frac_per_mille;
+    ap.keep_first = budget->keep_first;
+    ap.keep_last = budget->keep_last;
+  } else {
+    e = sv::launch_topk(sp, st);
+    if (e != hipSuccess) return from_hip(e, what);
+  }
+  return from_hip(sv::launch_attn(ap, bf16, st), what);
 }
 
 sv_status sv_reuse_indices(const sv_shape* shape, int32_t k_max, const int32_t* prev_idx,

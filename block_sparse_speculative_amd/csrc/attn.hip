@@ -6,21 +6,27 @@
 // Work unit = (sequence b, KV head g). Its rows are the T x G (draft token, query
 // head of the group) pairs, padded to RP in {16, 32, 64, 128}; its keys are the
 // valid tokens of the selected blocks plus the T draft tokens (draft t sees drafts
-// 0..t). Keys are cut into tiles of TT tokens (a tile never spans two blocks); split
-// s of S takes a contiguous range of context tiles, and one more workgroup per unit
-// takes the draft tile alone (with S == 1 the single split takes it first).
+// 0..t). Keys are cut into tiles of TT tokens (a tile never spans two blocks). The
+// k_max * (bs / TT) tile slots of a unit are cut into S balanced contiguous ranges
+// fixed by k_max alone, so a split knows which selected positions it owns before
+// the selected count arrives; slots at or past the count are skipped. One more
+// workgroup per unit takes the draft tile alone (with S == 1 the single split
+// takes it first).
 //
-// Prologue: the sequence's block-table row, the split's block indices and the
-// query fragments are requested together, so the chain before the first tile is
-// one dependent load (selected count -> indices).
+// Prologue: the block-table row, the split's block indices (or, in the fused
+// select mode, the unit's block scores), the context length and the query
+// fragments are requested together, so one round trip precedes the first tile.
+// In the fused select mode one wavefront of every context split runs the exact
+// budget + top-k of the unit from the scores (topk_wave.h) and keeps the positions
+// its split owns; split 0 also writes the unit's indices and count.
 //
 // Data movement: tiles stream HBM -> LDS through 16-byte LDS-DMA loads
-// (global_load_lds_dwordx4) into a ring of NBUF buffers (two workgroups share a CU),
-// so the next tile is in flight while one is computed. The DMA is issued from inline
-// assembly and waited for with explicit vmcnt counts (every tile is exactly LPW
-// loads per lane, and no other vector load sits in the loop). LDS rows are
-// XOR-swizzled in 16-byte chunks so the MFMA operand reads (16 lanes, 16 rows, one
-// chunk) hit distinct banks.
+// (global_load_lds_dwordx4) into a ring of NBUF buffers, so NBUF - 1 tiles are in
+// flight while one is computed (a 64 KB ring when two workgroups share a CU, else
+// 128 KB). The DMA is issued from inline assembly and waited for with explicit
+// vmcnt counts (every tile is exactly LPW loads per lane, and no other vector load
+// sits in the loop). LDS rows are XOR-swizzled in 16-byte chunks so the MFMA
+// operand reads (16 lanes, 16 rows, one chunk) hit distinct banks.
 //
 // Compute, per wave (16 rows, a subset of a tile's 32-token groups):
 //   S^T = K Q^T      (MFMA, M = tokens, N = rows, K = head dim)
@@ -36,14 +42,16 @@
 //
 // Merge of the partials of a unit:  O = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
 //  - S == 1: the workgroup normalises and writes the output itself.
-//  - small partial volume: each workgroup writes its partial with device-scope
-//    (sc1, coherent across XCDs) stores, waits for them, and takes a ticket from a
-//    per-unit arrival counter; the last workgroup to arrive reads the partials back
-//    with device-scope 16-byte loads and writes the output, then clears the counter.
-//    No cache writeback fence is needed because every access to the partials is
-//    device-scope.
 //  - otherwise merge_kernel combines the partials in a second launch.
+//
+// XCD placement: workgroups are dispatched to the 8 XCDs round-robin by linear id.
+// When the unit count is a multiple of 8, every kernel of the path (scoring,
+// attention, merge) maps unit u to linear ids congruent to u mod 8, so a unit's
+// scores, partials and indices are produced and consumed inside one XCD's L2 (a
+// handoff between kernels then costs no memory round trip). This is placement for
+// speed only; kernel boundaries keep the results coherent wherever a workgroup runs.
 #include "internal.h"
+#include "topk_wave.h"
 
 namespace sv {
 namespace {
@@ -52,11 +60,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
-typedef unsigned int u32x4v __attribute__((__vector_size__(16)));
-typedef unsigned int u32x2v __attribute__((__vector_size__(8)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kBtStageMax = 1024;    // block-table rows up to this length are staged in LDS
+static_assert(kWaveTopkMaxBlocks <= kBtStageMax, "the fused select mode reads the staged row");
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -98,29 +105,7 @@ __device__ __forceinline__ float sum_over_row_lanes(float x) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// Buffer resource over `bytes` bytes at `base` (raw, untyped); accesses past the
-// end return zero instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-// Device-scope (sc1) accesses: coherent across the XCDs' L2 caches without a cache
-// writeback, which is what lets the last split of a unit read its siblings'
-// partials.
-constexpr int kDeviceScope = 16;
-__device__ __forceinline__ void store_dev4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), r, off, 0, kDeviceScope);
-}
-__device__ __forceinline__ f32x4 load_dev4(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
-}
-__device__ __forceinline__ void store_dev2(__amdgpu_buffer_rsrc_t r, int off, float2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, v), r, off, 0, kDeviceScope);
-}
-__device__ __forceinline__ float2 load_dev2(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kDeviceScope));
-}
-
-template <bool BF16_, int D_, int TT_, int RP_>
+template <bool BF16_, int D_, int TT_, int RP_, int RING_KB_>
 struct Cfg {
   static constexpr bool BF16 = BF16_;
   static constexpr int D = D_;
@@ -142,12 +127,16 @@ struct Cfg {
   static constexpr int TILE_CH = KCH + VCH;
   static constexpr int TILE_BYTES = TILE_CH * 16;
   static constexpr int LPW = TILE_CH / NT;        // LDS-DMA loads per lane per tile
-  // Ring depth: two workgroups share a CU, so each keeps about 64 KB of tiles;
-  // vmcnt holds at most 63 outstanding loads.
+  // Ring depth: RING_KB of tiles (64 when two workgroups share a CU, 128 when one
+  // has it alone); vmcnt holds at most 63 outstanding loads.
+  static constexpr int RING_KB = RING_KB_;
+  // Workgroups per CU: two with a 64 KB ring (bf16; fp32 needs the registers of one).
+  static constexpr int MINB = (RING_KB <= 64 && BF16) ? 2 : 1;
   static constexpr int NBUF_VM = 1 + 63 / LPW;
-  static constexpr int NBUF_LDS = 65536 / TILE_BYTES;
-  static constexpr int NBUF = NBUF_VM < NBUF_LDS ? (NBUF_VM < 4 ? NBUF_VM : 4)
-                                                 : (NBUF_LDS < 4 ? NBUF_LDS : 4);
+  static constexpr int NBUF_LDS = RING_KB * 1024 / TILE_BYTES;
+  static constexpr int NBUF_CAP = 8;
+  static constexpr int NBUF = NBUF_VM < NBUF_LDS ? (NBUF_VM < NBUF_CAP ? NBUF_VM : NBUF_CAP)
+                                                 : (NBUF_LDS < NBUF_CAP ? NBUF_LDS : NBUF_CAP);
   static constexpr int KFC = NCHK / 4;            // K chunks per lane (a quarter row)
   static constexpr int VPM = BF16 ? 1 : 2;        // 16-byte V^T chunks per lane per md
   static constexpr int MERGE_BYTES = ((NTG - 1) * RP * D + 2 * NTG * RP) * 4;
@@ -159,6 +148,7 @@ struct Cfg {
   static constexpr int LDS_BYTES = FLAG_OFF + 16;
   static constexpr int BT_PER = (kBtStageMax + NT - 1) / NT;
   static_assert(NBUF >= 2, "need at least double buffering");
+  static_assert(RING_BYTES >= kTopkLdsBytes, "the top-k scratch lives in the ring");
   static_assert(TILE_CH % NT == 0, "tile must split evenly over the lanes");
   static_assert(KCH % 64 == 0, "a wave load must not straddle K and V");
   static_assert((NBUF - 1) * LPW < 64, "vmcnt range");
@@ -191,16 +181,19 @@ __device__ __forceinline__ uint4 lds_read16(const char* base, int chunk) {
   return *reinterpret_cast<const uint4*>(base + chunk * 16);
 }
 
-template <class C>
+// Waits until the tile that has n_after (0 .. NBUF-2) younger tiles in flight has
+// landed: at most n_after * LPW DMA loads may still be outstanding.
+template <class C, int N = C::NBUF - 2>
 __device__ __forceinline__ void wait_for_tile(int n_after) {
-  // n_after = DMA tiles issued after the one about to be used (0 .. NBUF-2).
-  if constexpr (C::NBUF >= 4) {
-    if (n_after >= 2) { wait_vmcnt<2 * C::LPW>(); return; }
+  if constexpr (N <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n_after >= N) {
+      wait_vmcnt<N * C::LPW>();
+      return;
+    }
+    wait_for_tile<C, N - 1>(n_after);
   }
-  if constexpr (C::NBUF >= 3) {
-    if (n_after >= 1) { wait_vmcnt<C::LPW>(); return; }
-  }
-  wait_vmcnt<0>();
 }
 
 // Running softmax state of one wave: O^T accumulators, row max (log2 units, scaled)
@@ -382,8 +375,8 @@ __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase
   }
 }
 
-template <class C>
-__global__ __launch_bounds__(C::NT, C::BF16 ? 2 : 1) void attn_kernel(AttnParams p) {
+template <class C, bool TOPK>
+__global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   constexpr int ES = C::ES;
   constexpr int D = C::D;
@@ -397,18 +390,51 @@ __global__ __launch_bounds__(C::NT, C::BF16 ? 2 : 1) void attn_kernel(AttnParams
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
-  const int split = blockIdx.x;
-  const int unit = blockIdx.y;
+  const int S = p.S;                  // context splits
+  const int NP = S > 1 ? S + 1 : 1;   // workgroups per unit (+1: the draft-only split)
+  // Linear workgroup id -> (unit, split); with xcd_group all workgroups of unit u
+  // have linear ids congruent to u mod 8 (same XCD).
+  int unit, split;
+  {
+    const int lin = blockIdx.x;
+    if (p.xcd_group) {
+      const int slot = lin >> 3;
+      unit = (slot / NP) * 8 + (lin & 7);
+      split = slot - (slot / NP) * NP;
+    } else {
+      unit = lin / NP;
+      split = lin - unit * NP;
+    }
+  }
   const int b = unit / p.Hkv;
   const int g = unit - b * p.Hkv;
-  const int S = p.S;                  // context splits
-  const int NP = S > 1 ? S + 1 : 1;   // partials per unit (+1: the draft-only split)
   const bool draft_split = S > 1 && split == S;
   const int tpb = p.bs / TT;
 
+  // Tile slots [s_begin, s_end) of this split, from k_max alone (balanced), and the
+  // selected positions q0 .. q0+nblk-1 they fall in.
+  const int n_slots = p.k_max * tpb;
+  int s_begin = 0, s_end = 0;
+  if (!draft_split) {
+    s_begin = static_cast<int>(static_cast<int64_t>(split) * n_slots / S);
+    s_end = static_cast<int>(static_cast<int64_t>(split + 1) * n_slots / S);
+  }
+  const int q0 = s_begin / tpb;
+  int nblk = s_end > s_begin ? (s_end - 1) / tpb - q0 + 1 : 0;
+  if (nblk > kAttnMaxBlocksPerSplit) nblk = kAttnMaxBlocksPerSplit;   // never for valid S
+
   // ---------------------------------------------------------------- prologue
-  // Requests that do not depend on the selected count go out first: the block-table
-  // row (staged in LDS when short enough) and the query fragments.
+  // Every request below is independent of the others: scalar context length (and
+  // selected count), the block-table row (staged in LDS when short enough), the
+  // split's block indices or the unit's scores, and the query fragments.
+  const cint_ptr s_ctx = (cint_ptr)(p.ctx_lens);
+  int ctx = s_ctx[b];
+  int nsel_in = 0;
+  if constexpr (!TOPK) {
+    const cint_ptr s_cnt = (cint_ptr)(p.cnt);
+    nsel_in = s_cnt[unit];
+  }
+
   const int32_t* gbt = p.block_table + static_cast<int64_t>(b) * p.NB;
   int* bt_lds = reinterpret_cast<int*>(smem + C::BT_OFF);
   const bool bt_staged = p.NB <= kBtStageMax;
@@ -419,6 +445,18 @@ __global__ __launch_bounds__(C::NT, C::BF16 ? 2 : 1) void attn_kernel(AttnParams
       const int i = tid + u * C::NT;
       btv[u] = i < p.NB ? gbt[i] : 0;
     }
+  }
+
+  int jv = -1;
+  const int32_t* gidx = TOPK ? nullptr : p.idx + static_cast<int64_t>(unit) * p.k_max + q0;
+  float sc[kWaveTopkMax / C::NT];
+  const bool selector = TOPK && !draft_split;   // the whole workgroup selects
+  if constexpr (TOPK) {
+    if (selector)
+      wg_topk_load<C::NWAVE>(p.scores + static_cast<int64_t>(unit) * p.NB,
+                             p.NB < kWaveTopkMax ? p.NB : kWaveTopkMax, sc);
+  } else {
+    if (tid < nblk) jv = gidx[tid];
   }
 
   // Row r of this wave's N-tile nt: (draft t, head hl) = (row / G, row % G).
@@ -442,35 +480,9 @@ __global__ __launch_bounds__(C::NT, C::BF16 ? 2 : 1) void attn_kernel(AttnParams
     }
   }
 
-  // Scalar: context length and selected count -> this split's tile range.
-  const cint_ptr s_ctx = (cint_ptr)(p.ctx_lens);
-  const cint_ptr s_cnt = (cint_ptr)(p.cnt);
-  int ctx = s_ctx[b];
   if (ctx < 0) ctx = 0;
   int nb = (ctx + p.bs - 1) / p.bs;
   if (nb > p.NB) nb = p.NB;
-  int nsel = s_cnt[unit];
-  if (nsel > p.k_max) nsel = p.k_max;
-  if (nsel < 0) nsel = 0;
-  const int nt_ctx = nsel * tpb;
-  const int tps = (nt_ctx + S - 1) / S;
-  int t_begin = draft_split ? nt_ctx : split * tps;
-  if (t_begin > nt_ctx) t_begin = nt_ctx;
-  int t_end = draft_split ? nt_ctx : t_begin + tps;
-  if (t_end > nt_ctx) t_end = nt_ctx;
-  // The draft tile: its own split when S > 1, else the single split's first tile.
-  const int has_draft = (S == 1 || draft_split) ? 1 : 0;
-  const int ntiles = (t_end - t_begin) + has_draft;
-  const int q0 = t_begin / tpb;
-  int nblk = t_end > t_begin ? (t_end - 1) / tpb - q0 + 1 : 0;
-  if (nblk > kAttnMaxBlocksPerSplit) nblk = kAttnMaxBlocksPerSplit;
-
-  // Block descriptors of this split: desc[q] = (physical block, valid tokens of the
-  // block), or (0, -1) for an index outside [0, nb) or a bad table entry.
-  int2* desc = reinterpret_cast<int2*>(smem + C::DESC_OFF);
-  const int32_t* gidx = p.idx + static_cast<int64_t>(unit) * p.k_max + q0;
-  int jv = -1;
-  if (tid < nblk) jv = gidx[tid];
   if (bt_staged) {
 #pragma unroll
     for (int u = 0; u < C::BT_PER; ++u) {
@@ -480,15 +492,69 @@ __global__ __launch_bounds__(C::NT, C::BF16 ? 2 : 1) void attn_kernel(AttnParams
   }
   wait_vmcnt<0>();
   lds_barrier();
-  for (int i = tid; i < nblk; i += C::NT) {
-    const int j = i == tid ? jv : gidx[i];
-    const bool jok = j >= 0 && j < nb;
-    const int pb = bt_staged ? bt_lds[jok ? j : 0] : gbt[jok ? j : 0];
-    const bool ok = jok && pb >= 0 && pb < p.P;
-    desc[i] = ok ? make_int2(pb, ctx - j * p.bs) : make_int2(0, -1);
+
+  // Block descriptors of this split: desc[q] = (physical block, valid tokens of the
+  // block) for selected position q0 + q, or (0, -1) for an index outside [0, nb) or
+  // a bad table entry.
+  int2* desc = reinterpret_cast<int2*>(smem + C::DESC_OFF);
+  // The table row is read from LDS when staged; the two sources stay in separate
+  // code paths so each compiles to its own instruction (a pointer chosen at run
+  // time between them would become a generic access that waits for all memory).
+  auto desc_of = [&](int j, int pb) {
+    const bool ok = j >= 0 && j < nb && pb >= 0 && pb < p.P;
+    return ok ? make_int2(pb, ctx - j * p.bs) : make_int2(0, -1);
+  };
+  auto clamp_j = [&](int j) { return (j >= 0 && j < nb) ? j : 0; };
+  int nsel;
+  if constexpr (TOPK) {
+    // Budget + exact top-k of the unit (the whole workgroup); this split keeps the
+    // positions it owns, split 0 publishes the indices and the count.
+    nsel = 0;
+    if (selector) {
+      int k = budget_blocks_dev(ctx, nb, p.dense_ctx, p.min_blocks, p.frac_per_mille);
+      if (k > p.k_max) k = p.k_max;
+      int32_t* idx_out = p.idx_out + static_cast<int64_t>(unit) * p.k_max;
+      const bool publish = split == 0;
+      // The table row is staged (the fused mode requires NB <= kBtStageMax); the LDS
+      // scratch is the start of the tile ring (no DMA is in flight yet).
+      int total = wg_topk_select<C::NWAVE>(
+          sc, nb, k, p.keep_first, p.keep_last, smem, [&](int j, int pos) {
+            if (pos >= q0 && pos < q0 + nblk) desc[pos - q0] = desc_of(j, bt_lds[clamp_j(j)]);
+            if (publish && pos < p.k_max) idx_out[pos] = j;
+          });
+      total = __builtin_amdgcn_readfirstlane(total);
+      if (total > p.k_max) total = p.k_max;
+      if (publish) {
+        for (int pos = total + tid; pos < p.k_max; pos += C::NT) idx_out[pos] = -1;
+        if (tid == 0) p.cnt_out[unit] = total;
+      }
+      nsel = total;
+    }
+    lds_barrier();
+  } else {
+    if (bt_staged) {
+      for (int i = tid; i < nblk; i += C::NT) {
+        const int j = i == tid ? jv : gidx[i];
+        desc[i] = desc_of(j, bt_lds[clamp_j(j)]);
+      }
+    } else {
+      for (int i = tid; i < nblk; i += C::NT) {
+        const int j = i == tid ? jv : gidx[i];
+        desc[i] = desc_of(j, gbt[clamp_j(j)]);
+      }
+    }
+    nsel = nsel_in;
+    wait_vmcnt<0>();   // nothing but the DMA stream is outstanding from here on
+    lds_barrier();
   }
-  wait_vmcnt<0>();   // nothing but the DMA stream is outstanding from here on
-  lds_barrier();
+  if (nsel > p.k_max) nsel = p.k_max;
+  if (nsel < 0) nsel = 0;
+  const int nt_ctx = nsel * tpb;
+  const int t_begin = s_begin < nt_ctx ? s_begin : nt_ctx;
+  const int t_end = s_end < nt_ctx ? s_end : nt_ctx;
+  // The draft tile: its own split when S > 1, else the single split's first tile.
+  const int has_draft = (S == 1 || draft_split) ? 1 : 0;
+  const int ntiles = (t_end - t_begin) + has_draft;
 
   const char* kpool = static_cast<const char*>(p.k_pool);
   const char* vpool = static_cast<const char*>(p.v_pool);
@@ -716,13 +782,11 @@ __global__ __launch_bounds__(C::NT, C::BF16 ? 2 : 1) void attn_kernel(AttnParams
   }
 
   // Partial of this split: O (unnormalised), running max (log2 units), denominator,
-  // written with device-scope stores.
-  const int part_bytes = NP * p.R * D * 4;
-  const __amdgpu_buffer_rsrc_t po =
-      make_rsrc(p.part_o + static_cast<int64_t>(unit) * NP * p.R * D, part_bytes);
-  const __amdgpu_buffer_rsrc_t pml =
-      make_rsrc(p.part_ml + static_cast<int64_t>(unit) * NP * p.R * 2, NP * p.R * 8);
+  // for merge_kernel. With XCD grouping the merge workgroups of the unit run on the
+  // same XCD and find the partials in its L2.
   if (writer) {
+    float* po = p.part_o + static_cast<int64_t>(unit) * NP * p.R * D;
+    float2* pml = reinterpret_cast<float2*>(p.part_ml) + static_cast<int64_t>(unit) * NP * p.R;
 #pragma unroll
     for (int nt = 0; nt < C::NN; ++nt) {
       const int row = row0 + nt * 16 + l16;
@@ -730,125 +794,67 @@ __global__ __launch_bounds__(C::NT, C::BF16 ? 2 : 1) void attn_kernel(AttnParams
       const int prow = split * p.R + row;
 #pragma unroll
       for (int md = 0; md < C::NMD; ++md)
-        store_dev4(po, (prow * D + md * 16 + 4 * g4) * 4, st.o[md][nt]);
-      if (g4 == 0) store_dev2(pml, prow * 8, make_float2(st.m[nt], st.l[nt]));
-    }
-  }
-  if (!p.fuse_merge) return;
-
-  // Arrival: every partial store of this workgroup has completed before the ticket
-  // is taken.
-  wait_vmcnt<0>();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  lds_barrier();
-  int* flag = reinterpret_cast<int*>(smem + C::FLAG_OFF);
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(p.tickets + unit, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (prev == static_cast<unsigned>(NP - 1)) ? 1 : 0;
-  }
-  lds_barrier();
-  if (*flag == 0) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (tid == 0)
-    __hip_atomic_store(p.tickets + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  // Last workgroup of the unit. Phase 1: per row, the weight of every partial,
-  // w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s', into LDS (and the row's LSE).
-  float* wts = reinterpret_cast<float*>(smem);     // [R][NP]
-  for (int row = tid; row < p.R; row += C::NT) {
-    float mmax = -__builtin_inff();
-    for (int s2 = 0; s2 < NP; ++s2) mmax = fmaxf(mmax, load_dev2(pml, (s2 * p.R + row) * 8).x);
-    const float msafe = mmax == -__builtin_inff() ? 0.0f : mmax;
-    float l = 0.0f;
-    for (int s2 = 0; s2 < NP; ++s2) {
-      const float2 ml = load_dev2(pml, (s2 * p.R + row) * 8);
-      const float w = __builtin_amdgcn_exp2f(ml.x - msafe);
-      wts[row * NP + s2] = w;
-      l += w * ml.y;
-    }
-    const float inv = 1.0f / l;
-    for (int s2 = 0; s2 < NP; ++s2) wts[row * NP + s2] *= inv;
-    if (p.lse) {
-      const int t = row / p.G;
-      const int h = g * p.G + (row - t * p.G);
-      p.lse[(static_cast<int64_t>(b) * p.T + t) * p.Hq + h] = (mmax + __builtin_log2f(l)) * kLn2;
-    }
-  }
-  lds_barrier();
-  // Phase 2: out = sum_s w_s O_s, 4 head dims per thread, all loads of an item in
-  // flight together.
-  for (int i4 = tid; i4 * 4 < p.R * D; i4 += C::NT) {
-    const int row = (i4 * 4) / D;
-    const int dim = i4 * 4 - row * D;
-    f32x4 os[kAttnFusedMaxPartials];
-#pragma unroll
-    for (int s2 = 0; s2 < kAttnFusedMaxPartials; ++s2)
-      if (s2 < NP) os[s2] = load_dev4(po, ((s2 * p.R + row) * D + dim) * 4);
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s2 = 0; s2 < kAttnFusedMaxPartials; ++s2)
-      if (s2 < NP) o += wts[row * NP + s2] * os[s2];
-    const int t = row / p.G;
-    const int h = g * p.G + (row - t * p.G);
-    const int64_t off = ((static_cast<int64_t>(b) * p.T + t) * p.Hq + h) * D + dim;
-    if constexpr (C::BF16) {
-      bf16x4_t w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = static_cast<__bf16>(o[e]);
-      *reinterpret_cast<bf16x4_t*>(static_cast<char*>(p.out) + off * 2) = w;
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = o;
+        *reinterpret_cast<f32x4*>(po + static_cast<int64_t>(prow) * D + md * 16 + 4 * g4) =
+            st.o[md][nt];
+      if (g4 == 0) pml[prow] = make_float2(st.m[nt], st.l[nt]);
     }
   }
 }
 
-// Combine the S partials of every (unit, row) in one pass over the splits, eight
-// splits per batch of loads (a running max rescales the accumulated sum). One
-// thread per 4 head dims.
+// Combine the S partials of every (unit, row) in one pass over the splits, sixteen
+// splits per batch of loads (a running max rescales the accumulated sum across
+// batches). One thread per 4 head dims.
 constexpr int kMergeThreads = 64;
 
 template <bool BF16>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
-  const int unit = blockIdx.y;
-  const int i4 = blockIdx.x * kMergeThreads + threadIdx.x;
   const int D = p.D;
+  const int per_unit = (p.R * D / 4 + kMergeThreads - 1) / kMergeThreads;   // workgroups
+  int unit, blk;
+  {
+    const int lin = blockIdx.x;
+    if (p.xcd_group) {
+      const int slot = lin >> 3;
+      unit = (slot / per_unit) * 8 + (lin & 7);
+      blk = slot - (slot / per_unit) * per_unit;
+    } else {
+      unit = lin / per_unit;
+      blk = lin - unit * per_unit;
+    }
+  }
+  const int i4 = blk * kMergeThreads + threadIdx.x;
   if (i4 * 4 >= p.R * D) return;
   const int row = (i4 * 4) / D;
   const int dim = i4 * 4 - row * D;
   const int S = p.S + 1;   // context splits plus the draft split
   const int64_t base = static_cast<int64_t>(unit) * S * p.R + row;
-  constexpr int BATCH = 8;
+  // Loads of a batch are unconditional (an index past the last partial re-reads the
+  // last one) and masked afterwards, so they are all in flight together.
+  constexpr int BATCH = 16;
   float mrun = -__builtin_inff(), l = 0.0f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += BATCH) {
-    float m[BATCH], ls[BATCH];
+    float2 ml[BATCH];
     f32x4 os[BATCH];
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
-      if (s0 + k < S) {
-        const int64_t pr = base + static_cast<int64_t>(s0 + k) * p.R;
-        const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + pr * 2);
-        m[k] = ml.x;
-        ls[k] = ml.y;
-        os[k] = *reinterpret_cast<const f32x4*>(p.part_o + pr * D + dim);
-      } else {
-        m[k] = -__builtin_inff();
-        ls[k] = 0.0f;
-        os[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      const int sk = s0 + k < S ? s0 + k : S - 1;
+      const int64_t pr = base + static_cast<int64_t>(sk) * p.R;
+      ml[k] = *reinterpret_cast<const float2*>(p.part_ml + pr * 2);
+      os[k] = *reinterpret_cast<const f32x4*>(p.part_o + pr * D + dim);
     }
     float mb = mrun;
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k) mb = fmaxf(mb, m[k]);
+    for (int k = 0; k < BATCH; ++k)
+      if (s0 + k < S) mb = fmaxf(mb, ml[k].x);
     const float msafe = mb == -__builtin_inff() ? 0.0f : mb;
     const float a = __builtin_amdgcn_exp2f(mrun - msafe);
     l *= a;
     o *= a;
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
-      const float w = __builtin_amdgcn_exp2f(m[k] - msafe);
-      l += w * ls[k];
+      const float w = s0 + k < S ? __builtin_amdgcn_exp2f(ml[k].x - msafe) : 0.0f;
+      l += w * ml[k].y;
       o += w * os[k];
     }
     mrun = mb;
@@ -873,18 +879,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
 
 template <class C>
 hipError_t launch_cfg(const AttnParams& p, hipStream_t stream) {
-  dim3 grid(p.S > 1 ? p.S + 1 : 1, p.B * p.Hkv);
-  hipLaunchKernelGGL(attn_kernel<C>, grid, dim3(C::NT), 0, stream, p);
+  dim3 grid((p.S > 1 ? p.S + 1 : 1) * p.B * p.Hkv);
+  if (p.scores)
+    hipLaunchKernelGGL((attn_kernel<C, true>), grid, dim3(C::NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_kernel<C, false>), grid, dim3(C::NT), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool BF16, int D, int TT, int RP>
+hipError_t launch_ring(const AttnParams& p, hipStream_t stream) {
+  if (attn_ring_kb(p.S, p.B * p.Hkv, p.R, BF16) == 128)
+    return launch_cfg<Cfg<BF16, D, TT, RP, 128>>(p, stream);
+  return launch_cfg<Cfg<BF16, D, TT, RP, 64>>(p, stream);
 }
 
 template <bool BF16, int D, int TT>
 hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
   switch (attn_padded_rows(p.R)) {
-    case 16: return launch_cfg<Cfg<BF16, D, TT, 16>>(p, stream);
-    case 32: return launch_cfg<Cfg<BF16, D, TT, 32>>(p, stream);
-    case 64: return launch_cfg<Cfg<BF16, D, TT, 64>>(p, stream);
-    default: return launch_cfg<Cfg<BF16, D, TT, 128>>(p, stream);
+    case 16: return launch_ring<BF16, D, TT, 16>(p, stream);
+    case 32: return launch_ring<BF16, D, TT, 32>(p, stream);
+    case 64: return launch_ring<BF16, D, TT, 64>(p, stream);
+    default: return launch_ring<BF16, D, TT, 128>(p, stream);
   }
 }
 
@@ -902,16 +918,11 @@ hipError_t launch_dtype(const AttnParams& p, hipStream_t stream) {
 
 }  // namespace
 
-bool attn_fuses_merge(int splits, int rows, int head_dim) {
-  return splits > 1 && splits + 1 <= kAttnFusedMaxPartials &&
-         static_cast<int64_t>(splits + 1) * rows * head_dim * 4 <= kAttnFusedMergeBytes;
-}
-
 hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
   hipError_t e = bf16 ? launch_dtype<true>(p, stream) : launch_dtype<false>(p, stream);
-  if (e != hipSuccess || p.S == 1 || p.fuse_merge) return e;
-  dim3 grid((p.R * p.D / 4 + kMergeThreads - 1) / kMergeThreads, p.B * p.Hkv);
+  if (e != hipSuccess || p.S == 1) return e;
+  dim3 grid((p.R * p.D / 4 + kMergeThreads - 1) / kMergeThreads * p.B * p.Hkv);
   if (bf16)
     hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(kMergeThreads), 0, stream, p);
   else

@@ -29,6 +29,7 @@ struct SelectParams {
   int32_t* idx;
   int32_t* cnt;
   float* scores;        // [B, Hkv, NB] (user buffer or workspace)
+  int32_t xcd_group;    // nonzero: the workgroups of unit u have linear ids = u mod 8
   int32_t scores_requested;   // nonzero: write scores even where every block is kept
   int32_t B, Hq, Hkv, G, D, T, bs, NB, P, k_max;
   int32_t dense_ctx, min_blocks, frac_per_mille, keep_first, keep_last;
@@ -42,18 +43,21 @@ struct AttnParams {
   const void* v_pool;
   const int32_t* block_table;
   const int32_t* ctx_lens;
-  const int32_t* idx;
-  const int32_t* cnt;
+  const int32_t* idx;   // selected blocks [units, k_max] (read unless `scores` is set)
+  const int32_t* cnt;   // selected counts [units]
+  const float* scores;  // fused select mode: block scores [units, NB], else null
+  int32_t* idx_out;     // fused select mode: indices / counts written by split 0
+  int32_t* cnt_out;
   void* out;
   float* lse;
   float* part_o;        // [units, S+1, R, D] unnormalised partial outputs
   float* part_ml;       // [units, S+1, R, 2]  (running max in log2 units, denominator)
-  uint32_t* tickets;    // [units] arrival counters of the fused merge, zero between calls
-  int32_t fuse_merge;   // nonzero: the last split of a unit merges (no merge kernel)
+  int32_t xcd_group;    // nonzero: the workgroups of unit u have linear ids = u mod 8
   int32_t B, Hq, Hkv, G, D, T, bs, NB, P, k_max;
   int32_t S;            // context splits (a draft-only split is added when S > 1)
   int32_t R;
   float scale_log2;     // softmax scale * log2(e), > 0
+  int32_t dense_ctx, min_blocks, frac_per_mille, keep_first, keep_last;   // fused select
 };
 
 struct ReuseParams {
@@ -69,10 +73,10 @@ struct ReuseParams {
 // Each returns hipSuccess or the launch error; shapes are validated by the caller.
 
 hipError_t launch_block_repr(const ReprParams& p, bool bf16, hipStream_t stream);
-hipError_t launch_select(const SelectParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_select(const SelectParams& p, bool bf16, hipStream_t stream);   // score + top-k
+hipError_t launch_score(const SelectParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_topk(const SelectParams& p, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream);
-// Whether the attention kernel merges its splits itself (small partial volume).
-bool attn_fuses_merge(int splits, int rows, int head_dim);
 hipError_t launch_reuse(const ReuseParams& p, hipStream_t stream);
 
 // Tokens per attention tile (a tile never spans two blocks): 64 for bf16 blocks of
@@ -81,19 +85,32 @@ inline int attn_tile_tokens(int block_size, bool bf16) {
   return (bf16 && block_size >= 64) ? 64 : 32;
 }
 
+constexpr int kAttnCUs = 256;        // compute units of the MI355X
+constexpr int kXcds = 8;             // XCDs; workgroups are dispatched round-robin over them
+
+// Whether the per-unit kernels can place each unit on one XCD.
+inline bool xcd_groupable(int units) { return units % kXcds == 0; }
+
+// LDS ring of one attention workgroup in KB: 128 when a workgroup has its CU to
+// itself (the grid has at most one per CU, 128 padded rows = 8 waves, or fp32,
+// whose registers allow one), else 64 so that two workgroups share a CU.
+inline int attn_ring_kb(int splits, int units, int rows, bool bf16) {
+  const int64_t wgs = static_cast<int64_t>(splits > 1 ? splits + 1 : 1) * units;
+  return (!bf16 || wgs <= kAttnCUs || rows > 64) ? 128 : 64;
+}
+
 // Padded row count of the (draft token x GQA head) tile.
 inline int attn_padded_rows(int rows) {
   return rows <= 16 ? 16 : rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
 }
 
 constexpr int kSelectChunk = 128;     // blocks scored by one select workgroup
+// Longest block-table row whose top-k one wavefront does in registers (the fused
+// select-and-attend mode needs it; longer rows take the separate top-k kernel).
+constexpr int kWaveTopkMaxBlocks = 1024;
 // Most selected blocks one attention split stages descriptors for (the split count
 // is raised so that no split covers more).
 constexpr int kAttnMaxBlocksPerSplit = 1024;
-// Largest per-unit partial volume (S x rows x head_dim x 4 bytes) merged by the
-// last attention workgroup of the unit instead of a separate merge launch.
-constexpr int64_t kAttnFusedMergeBytes = 160 * 1024;
-constexpr int kAttnFusedMaxPartials = 17;
 constexpr int kSelectThreads = 256;
 
 }  // namespace sv

@@ -11,10 +11,14 @@
 //                per lane, D/4 lanes per block, shuffle reduction in a fixed order).
 //                Sequences whose budget keeps every block are skipped unless the
 //                caller asked for the scores.
-//  topk_kernel   grid = (Hkv, B): budget, then an LDS radix select on
-//                order-preserving 32-bit keys and an ascending compaction of the
-//                chosen indices with block-wide scans.
+//  top-k         grid = (Hkv, B): budget, then
+//                 - NB <= 1024: the keys spread over the registers of four
+//                   wavefronts, LDS radix select with a single-register finish and
+//                   ballot compaction (topk_wave.h);
+//                 - larger NB: an LDS radix select on the same order-preserving
+//                   keys and an ascending compaction with block-wide scans.
 #include "internal.h"
+#include "topk_wave.h"
 
 namespace sv {
 namespace {
@@ -24,16 +28,6 @@ constexpr int NWAVE = NT / 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
-}
-
-// Order-preserving map of a float score to an unsigned key: larger score, larger
-// key. -0 and +0 map to the same key; NaN maps to the key of -inf (the lowest
-// rank, tied with -inf). Key 0 is reserved for "not a candidate".
-__device__ __forceinline__ uint32_t score_key(float s) {
-  if (s != s) s = -__builtin_inff();
-  if (s == 0.0f) s = 0.0f;
-  const uint32_t u = __float_as_uint(s);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Block-wide exclusive scan of one int per thread; returns the prefix and sets
@@ -61,11 +55,8 @@ __device__ int block_exclusive_scan(int v, int* total, int* scratch) {
   return before + x - v;
 }
 
-__device__ __forceinline__ int budget_blocks_dev(const SelectParams& p, int ctx, int nb) {
-  if (ctx <= p.dense_ctx) return nb;
-  int k = (p.frac_per_mille * nb + 999) / 1000;
-  if (k < p.min_blocks) k = p.min_blocks;
-  return k < nb ? k : nb;
+__device__ __forceinline__ int budget_of(const SelectParams& p, int ctx, int nb) {
+  return budget_blocks_dev(ctx, nb, p.dense_ctx, p.min_blocks, p.frac_per_mille);
 }
 
 template <typename E, int D>
@@ -73,9 +64,23 @@ __global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int unit = b * p.Hkv + g;
+  // Linear workgroup id -> (unit, chunk); with xcd_group the workgroups of unit u
+  // have linear ids congruent to u mod 8, the XCD its attention workgroups use.
+  const int nchunk = (p.NB + kSelectChunk - 1) / kSelectChunk;
+  int unit, chunk;
+  {
+    const int lin = blockIdx.x;
+    if (p.xcd_group) {
+      const int slot = lin >> 3;
+      unit = (slot / nchunk) * 8 + (lin & 7);
+      chunk = slot - (slot / nchunk) * nchunk;
+    } else {
+      unit = lin / nchunk;
+      chunk = lin - unit * nchunk;
+    }
+  }
+  const int b = unit / p.Hkv;
+  const int g = unit - b * p.Hkv;
   int ctx = p.ctx_lens[b];
   if (ctx < 0) ctx = 0;
   int nb = (ctx + p.bs - 1) / p.bs;
@@ -89,23 +94,14 @@ __global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
   constexpr int PASSES = kSelectChunk / (NWAVE * BPW);
   const int sub = lane / LPB;
   const int li = lane % LPB;
-  const int j0 = static_cast<int>(blockIdx.x) * kSelectChunk;
+  const int j0 = chunk * kSelectChunk;
   // A sequence whose budget keeps every block needs no scores.
-  const bool dense = budget_blocks_dev(p, ctx, nb) >= nb;
+  const bool dense = budget_of(p, ctx, nb) >= nb;
   if (j0 < nb && (!dense || p.scores_requested)) {
     const E* q = static_cast<const E*>(p.q) + static_cast<int64_t>(b) * p.T * p.Hq * D;
-    float qs[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int hl = 0; hl < p.G; ++hl) {
-      const E* qh = q + static_cast<int64_t>(g * p.G + hl) * D + 4 * li;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v;
-        if constexpr (sizeof(E) == 2) v = bf16_to_f32(qh[e]); else v = qh[e];
-        qs[e] += v;
-      }
-    }
-    // All block-table loads first, then all representative loads: no branch
-    // between them, so every load of the workgroup is in flight at once.
+    // Block-table loads first, then the query loads, then all representative loads
+    // (a bad entry re-reads block 0), then the dot products: no load waits for an
+    // unrelated one.
     float4 r[PASSES];
     int jj[PASSES], ph[PASSES];
 #pragma unroll
@@ -114,12 +110,31 @@ __global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
       jj[u] = j;
       ph[u] = bt[j < nb ? j : 0];
     }
+    // Sum of the group's first-draft query vectors, 8 heads per batch of loads. The
+    // loads are unconditional (a head index past the group re-reads the last head)
+    // and masked afterwards, so none waits for another.
+    float qs[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int h0 = 0; h0 < p.G; h0 += 8) {
+      float v[8][4];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int hl = h0 + k < p.G ? h0 + k : p.G - 1;
+        const E* qh = q + static_cast<int64_t>(g * p.G + hl) * D + 4 * li;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (sizeof(E) == 2) v[k][e] = bf16_to_f32(qh[e]); else v[k][e] = qh[e];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qs[e] += h0 + k < p.G ? v[k][e] : 0.0f;
+    }
 #pragma unroll
     for (int u = 0; u < PASSES; ++u) {
       const bool ok = jj[u] < nb && ph[u] >= 0 && ph[u] < p.P;
       r[u] = *reinterpret_cast<const float4*>(
           p.repr_pool + (static_cast<int64_t>(ok ? ph[u] : 0) * p.Hkv + g) * D + 4 * li);
-      if (!ok) r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < PASSES; ++u) {
@@ -129,12 +144,41 @@ __global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
       d = __builtin_fmaf(qs[3], r[u].w, d);
 #pragma unroll
       for (int off = LPB / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off, 64);
+      const bool ok = ph[u] >= 0 && ph[u] < p.P;
+      d = ok ? d : 0.0f;
       if (li == 0 && jj[u] < nb) sc[jj[u]] = d;
     }
   }
 
 }
 
+// One workgroup of kTopkWaves wavefronts per unit (NB <= 1024).
+constexpr int kTopkWaves = 4;
+__global__ __launch_bounds__(kTopkWaves * 64) void topk_wave_kernel(SelectParams p) {
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int unit = b * p.Hkv + g;
+  __shared__ __attribute__((aligned(16))) char lds[kTopkLdsBytes];
+  float s[kWaveTopkMax / (64 * kTopkWaves)];
+  wg_topk_load<kTopkWaves>(p.scores + static_cast<int64_t>(unit) * p.NB, p.NB, s);
+  int ctx = p.ctx_lens[b];
+  if (ctx < 0) ctx = 0;
+  int nb = (ctx + p.bs - 1) / p.bs;
+  if (nb > p.NB) nb = p.NB;
+  int k = budget_of(p, ctx, nb);
+  if (k > p.k_max) k = p.k_max;
+  int32_t* out = p.idx + static_cast<int64_t>(unit) * p.k_max;
+  int total = wg_topk_select<kTopkWaves>(s, nb, k, p.keep_first, p.keep_last, lds,
+                                         [&](int j, int pos) {
+                                           if (pos < p.k_max) out[pos] = j;
+                                         });
+  if (total > p.k_max) total = p.k_max;
+  for (int pos = total + tid; pos < p.k_max; pos += kTopkWaves * 64) out[pos] = -1;
+  if (tid == 0) p.cnt[unit] = total;
+}
+
+// One workgroup per unit, keys in LDS (any NB).
 __global__ __launch_bounds__(NT) void topk_kernel(SelectParams p) {
   extern __shared__ uint32_t keys[];           // [NB]
   __shared__ int hist[256];
@@ -152,11 +196,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams p) {
   const float* sc = p.scores + static_cast<int64_t>(unit) * p.NB;
 
   // ------------------------------------------------------------ budget + top-k
-  int k = budget_blocks_dev(p, ctx, nb);
+  int k = budget_of(p, ctx, nb);
   if (k > p.k_max) k = p.k_max;
   int32_t* out = p.idx + static_cast<int64_t>(unit) * p.k_max;
   if (k >= nb) {
-    if (tid == 0) p.cnt[unit] = nb;
+    if (tid == 0) p.cnt[unit] = nb < p.k_max ? nb : p.k_max;
     for (int pos = tid; pos < p.k_max; pos += NT) out[pos] = pos < nb ? pos : -1;
     return;
   }
@@ -244,9 +288,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams p) {
 
 }  // namespace
 
-hipError_t launch_select(const SelectParams& p, bool bf16, hipStream_t stream) {
+hipError_t launch_score(const SelectParams& p, bool bf16, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
-  dim3 grid((p.NB + kSelectChunk - 1) / kSelectChunk, p.Hkv, p.B);
+  dim3 grid((p.NB + kSelectChunk - 1) / kSelectChunk * p.Hkv * p.B);
   if (bf16) {
     if (p.D == 128)
       hipLaunchKernelGGL((score_kernel<uint16_t, 128>), grid, dim3(NT), 0, stream, p);
@@ -258,11 +302,24 @@ hipError_t launch_select(const SelectParams& p, bool bf16, hipStream_t stream) {
     else
       hipLaunchKernelGGL((score_kernel<float, 64>), grid, dim3(NT), 0, stream, p);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t lds = static_cast<size_t>(p.NB) * sizeof(uint32_t);
-  hipLaunchKernelGGL(topk_kernel, dim3(p.Hkv, p.B), dim3(NT), lds, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_topk(const SelectParams& p, hipStream_t stream) {
+  if (p.B == 0) return hipSuccess;
+  static_assert(kWaveTopkMax == kWaveTopkMaxBlocks, "one wave holds a whole row");
+  if (p.NB <= kWaveTopkMax) {
+    hipLaunchKernelGGL(topk_wave_kernel, dim3(p.Hkv, p.B), dim3(kTopkWaves * 64), 0, stream, p);
+  } else {
+    const size_t lds = static_cast<size_t>(p.NB) * sizeof(uint32_t);
+    hipLaunchKernelGGL(topk_kernel, dim3(p.Hkv, p.B), dim3(NT), lds, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectParams& p, bool bf16, hipStream_t stream) {
+  const hipError_t e = launch_score(p, bf16, stream);
+  return e != hipSuccess ? e : launch_topk(p, stream);
 }
 
 }  // namespace sv

@@ -64,8 +64,9 @@ class Workspaces:
         self.sel = torch.empty(max(L.select_workspace_bytes(shape, k_max), 1), dtype=torch.uint8,
                                device=device)
         n = L.attn_workspace_bytes(shape, k_max, num_splits)
-        # zero-filled once: the attention workspace starts with arrival counters
-        self.attn = torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+        self.attn = torch.empty(n, dtype=torch.uint8, device=device) if n else None
+        self.fused = torch.empty(L.select_and_attend_workspace_bytes(shape, k_max, num_splits),
+                                 dtype=torch.uint8, device=device)
         self.num_splits = num_splits
 
 
@@ -73,6 +74,13 @@ def select(shape, budget, q, pool: Pool, block_table, ctx_lens, k_max, idx, cnt,
            scores: Optional[torch.Tensor] = None):
     L.select_blocks(shape, budget, q, pool.reps, block_table, ctx_lens, k_max, idx, cnt,
                     scores=scores, ws=ws.sel)
+
+
+def select_and_attend(shape, budget, q, k_draft, v_draft, pool: Pool, block_table, ctx_lens,
+                      k_max, scale, idx, cnt, out, ws: Workspaces, lse=None):
+    L.select_and_attend(shape, budget, q, pool.reps, k_draft, v_draft, pool.k, pool.v,
+                        block_table, ctx_lens, k_max, scale, idx, cnt, out, lse=lse,
+                        ws=ws.fused, num_splits=ws.num_splits)
 
 
 def attend(shape, q, k_draft, v_draft, pool: Pool, block_table, ctx_lens, idx, cnt, k_max, scale,

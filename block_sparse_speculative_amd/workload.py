@@ -2,8 +2,12 @@
 built on the device through sv_block_repr, plus the index/output buffers of a pass.
 
 A verification pass over the instance runs, for every layer, either block selection
-(sv_select_blocks) or inter-layer reuse (sv_reuse_indices), then the sparse
-multi-draft attention (sv_sparse_verify_attn).
+or inter-layer reuse, then the sparse multi-draft attention. Two ways to run it:
+ - separate calls: sv_select_blocks or sv_reuse_indices (a copy of the previous
+   layer's indices), then sv_sparse_verify_attn;
+ - fused (the fast path): sv_select_and_attend on selecting layers, and on reuse
+   layers sv_sparse_verify_attn reading the previous layer's index buffers
+   themselves (the layer's idx / cnt ARE the previous layer's tensors).
 """
 
 from __future__ import annotations
@@ -35,7 +39,8 @@ class Instance:
     def __init__(self, w: synth.Workload, seed: int = 0, device="cuda", num_layers: Optional[int] = None,
                  ctx_lens: Optional[List[int]] = None, paged: Optional[bool] = None,
                  num_splits: int = 0, with_lse: bool = True, nan_pool: bool = False,
-                 k_max: Optional[int] = None, append_chunk: int = 0, progress=None):
+                 k_max: Optional[int] = None, append_chunk: int = 0, progress=None,
+                 fused: bool = False):
         if paged is not None:
             w = w.with_(paged=paged)
         self.w = w
@@ -54,6 +59,7 @@ class Instance:
         self.scale = synth.softmax_scale(w)
         self.ws = PL.Workspaces(self.shape, self.k_max, num_splits, self.device)
         self.num_splits = L.attn_num_splits(self.shape, self.k_max, num_splits)
+        self.fused = fused
         n_layers = w.num_layers if num_layers is None else num_layers
         B, T, Hq, Hkv, D = w.num_seqs, w.num_draft, w.num_q_heads, w.num_kv_heads, w.head_dim
         self.layers: List[Layer] = []
@@ -63,10 +69,14 @@ class Instance:
             PL.fill_pool(self.shape, pool, x["k_ctx"], x["v_ctx"], self.ctx_lens, self.table,
                          chunk=append_chunk)
             reuse = w.reuse_odd_layers and l % 2 == 1
+            if reuse and fused:
+                idx, cnt = self.layers[l - 1].idx, self.layers[l - 1].cnt
+            else:
+                idx = torch.full((B, Hkv, self.k_max), -7, dtype=torch.int32, device=self.device)
+                cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device=self.device)
             self.layers.append(Layer(
                 q=x["q"], k_draft=x["k_draft"], v_draft=x["v_draft"], pool=pool, reuse=reuse,
-                idx=torch.full((B, Hkv, self.k_max), -7, dtype=torch.int32, device=self.device),
-                cnt=torch.full((B, Hkv), -7, dtype=torch.int32, device=self.device),
+                idx=idx, cnt=cnt,
                 out=torch.empty((B, T, Hq, D), dtype=w.torch_dtype, device=self.device),
                 lse=torch.empty((B, T, Hq), dtype=torch.float32, device=self.device)
                 if with_lse else None))
@@ -93,8 +103,16 @@ class Instance:
                   ly.cnt, self.k_max, self.scale, ly.out, self.ws, lse=ly.lse)
 
     def run_layer(self, l: int):
-        self.select_or_reuse(l)
-        self.attend(l)
+        ly = self.layers[l]
+        if not self.fused:
+            self.select_or_reuse(l)
+            self.attend(l)
+        elif ly.reuse:
+            self.attend(l)        # idx / cnt alias the previous layer's
+        else:
+            PL.select_and_attend(self.shape, self.budget, ly.q, ly.k_draft, ly.v_draft, ly.pool,
+                                 self.table, self.ctx, self.k_max, self.scale, ly.idx, ly.cnt,
+                                 ly.out, self.ws, lse=ly.lse)
 
     def step(self):
         for l in range(len(self.layers)):

@@ -139,10 +139,10 @@ size_t sv_select_workspace_bytes(const sv_shape* shape, int32_t k_max);
  * by score (ties to the lower index; NaN ranks lowest).
  *   q          [B, T, Hq, D] dtype; only draft token 0 is read
  *   idx        [B, Hkv, k_max] int32 out: ascending logical indices, padded with -1
- *   cnt        [B, Hkv]        int32 out: number of selected blocks (= k)
+ *   cnt        [B, Hkv]        int32 out: number of selected blocks (= min(k, k_max))
  *   scores     [B, Hkv, NB]    float32 out, optional (NULL): the block scores
- * k_max must be >= k for every sequence (use sv_budget_blocks); a larger k is
- * clamped to k_max. `ws` must hold sv_select_workspace_bytes() bytes (scratch for
+ * k_max must be >= k for every sequence (use sv_budget_blocks); otherwise only
+ * the first k_max selected blocks (in ascending order) are kept. `ws` must hold sv_select_workspace_bytes() bytes (scratch for
  * the scores when `scores` is NULL); its contents need no initialisation. Two
  * kernels are enqueued (scoring, then budget + top-k). */
 sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const void* q,
@@ -152,7 +152,9 @@ sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const
                            void* stream);
 
 /* Number of KV splits sv_sparse_verify_attn uses: `num_splits` if > 0 (clamped to
- * the work available), else the library's choice for this shape. With more than one
+ * the work available), else the library's choice for this shape. The k_max * (bs/TT)
+ * tile slots of a (sequence, KV head) are cut into that many balanced ranges, where
+ * TT = 64 tokens for bf16 blocks of 64 or more tokens, else 32. With more than one
  * split, one extra workgroup per (sequence, KV head) handles the draft tokens. */
 int32_t sv_attn_num_splits(const sv_shape* shape, int32_t k_max, int32_t num_splits);
 
@@ -174,17 +176,44 @@ size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num
  *   ctx_lens [B] int32; idx [B, Hkv, k_max]; cnt [B, Hkv]   (device)
  *   out [B, T, Hq, D] dtype; lse [B, T, Hq] float32 or NULL
  * num_splits: 0 = library choice, else the number of KV splits (see
- * sv_attn_num_splits). `ws` must hold sv_attn_workspace_bytes() bytes (may be
- * NULL when that is 0). Its first B*Hkv*4 bytes are per-unit arrival counters that
- * must be zero before the first call; every call that completes leaves them zero
- * (zero-fill the workspace once at allocation; do not share it between calls that
- * may run concurrently). scale must be finite and > 0. */
+ * sv_attn_num_splits). With more than one split the partial results go to `ws`
+ * (sv_attn_workspace_bytes() bytes, no initialisation needed; may be NULL when that
+ * is 0) and a second kernel merges them. Calls that may run concurrently must not
+ * share a workspace. scale must be finite and > 0. */
 sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,
                                 const void* v_draft, const void* k_pool, const void* v_pool,
                                 const int32_t* block_table, const int32_t* ctx_lens,
                                 const int32_t* idx, const int32_t* cnt, int32_t k_max,
                                 float scale, int32_t num_splits, void* out, float* lse,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace sv_select_and_attend needs for this shape. */
+size_t sv_select_and_attend_workspace_bytes(const sv_shape* shape, int32_t k_max,
+                                            int32_t num_splits);
+
+/* One selecting layer in one call: exactly sv_select_blocks followed by
+ * sv_sparse_verify_attn with the same arguments (same indices, counts, outputs and
+ * LSE), in fewer launches (tutorial page, "Core technique 1": representative
+ * scoring and top-k feed the sparse attention; sciencestack page, Figure 1
+ * caption: the first draft token's query picks the blocks that all drafts share).
+ *
+ * Launches: the scoring kernel, then the attention kernel, whose context workgroups
+ * each run the budget + top-k of their unit from the scores (one wavefront, exact,
+ * lowest index wins ties) before streaming their share of the selected blocks;
+ * split 0 of each unit writes idx / cnt. With NB > 1024 the separate top-k kernel
+ * runs between the two instead. Then the merge kernel when the splits need one.
+ *   arguments        as in sv_select_blocks and sv_sparse_verify_attn
+ *   idx, cnt         outputs (as sv_select_blocks writes them)
+ *   ws               sv_select_and_attend_workspace_bytes() bytes (attention partials,
+ *                    then the score scratch; no initialisation needed). Calls that
+ *                    may run concurrently must not share it. */
+sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
+                               const float* repr_pool, const void* k_draft, const void* v_draft,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* ctx_lens,
+                               int32_t k_max, float scale, int32_t num_splits, int32_t* idx,
+                               int32_t* cnt, void* out, float* lse, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* Inter-layer retrieval reuse (tutorial page, "Core technique 1": some layers take
  * the previous layer's retrieval result instead of selecting again; sciencestack

@@ -165,3 +165,37 @@ def test_binding_refuses_host_tensors():
     t = torch.zeros(1, 8, 8, 64, dtype=torch.int32)
     with pytest.raises(ValueError):
         sv.reuse_indices(shape, 64, t, t, t, t)
+
+
+def test_select_and_attend_rejects_before_launch():
+    lib = sv.lib()
+    shape = _shape()
+    good = ctypes.byref(sv.make_budget(4096, 64, 50))
+    need = sv.select_and_attend_workspace_bytes(shape, 64)
+    # the score scratch follows the attention workspace
+    assert need >= sv.attn_workspace_bytes(shape, 64) + 2 * 8 * 1024 * 4
+
+    def call(budget=good, ws=FAKE, ws_bytes=need, k_max=64, scale=0.1, q=FAKE, splits=0):
+        return lib.sv_select_and_attend(ctypes.byref(shape), budget, q, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, k_max, scale, splits, FAKE, FAKE, FAKE,
+                                        None, ws, ws_bytes, None)
+
+    assert call(budget=None) == 1
+    assert call(budget=ctypes.byref(sv.make_budget(4096, 1, 50, 1, 1))) == 2
+    assert call(ws=None, ws_bytes=0) == 4
+    assert call(ws_bytes=need - 1) == 4
+    assert call(q=None) == 1
+    assert call(k_max=0) == 2
+    assert call(scale=0.0) == 2
+    assert call(splits=-1) == 2
+    assert lib.sv_select_and_attend(ctypes.byref(_shape(head_dim=96)), good, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, FAKE, FAKE, FAKE, 64, 0.1, 0, FAKE, FAKE, FAKE,
+                                    None, FAKE, need, None) == 3
+
+
+def test_split_ranges_balanced_over_k_max():
+    # the tile slots of a unit are cut into balanced ranges: no split is left empty
+    shape = _shape(num_seqs=1)
+    for k_max in (64, 100, 1000):
+        for s in (3, 7, 10, 15):
+            assert sv.attn_num_splits(shape, k_max, s) == min(s, k_max)

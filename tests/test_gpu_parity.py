@@ -43,13 +43,16 @@ def run_and_check(inst, units=None, layers=None, check_reps=True, scores=False):
     units = _all_units(inst) if units is None else units
     gscores = None
     for l in range(n):
-        if scores and not inst.layers[l].reuse:
+        if inst.fused:
+            inst.run_layer(l)
+        elif scores and not inst.layers[l].reuse:
             gscores = torch.full((inst.w.num_seqs, inst.w.num_kv_heads, inst.shape.max_blocks_per_seq),
                                  float("nan"), dtype=torch.float32, device=inst.device)
             inst.select_or_reuse(l, scores=gscores)
         else:
             inst.select_or_reuse(l)
-        inst.attend(l)
+        if not inst.fused:
+            inst.attend(l)
     torch.cuda.synchronize()
     prev, stats_all = None, []
     for l in layers:
@@ -82,6 +85,9 @@ SMALL = {
                                  budget=(0, 12, 0, 1, 1), plant_count=4),
     "fp32_rows32_bs128": W["tiny"].with_(num_draft=8, block_size=128, ctx=(4500,),
                                          budget=(0, 8, 0, 1, 1)),
+    # more than 1024 blocks per row: LDS radix top-k, and the fused call's fallback
+    "long_table": W["llama32k"].with_(num_seqs=1, num_q_heads=8, num_kv_heads=2, block_size=32,
+                                      ctx=(40000,)),
 }
 
 
@@ -94,6 +100,25 @@ def test_small_workload_all_units(name, splits):
     PT.log(f"  resolved splits={inst.num_splits} k_max={inst.k_max}")
     run_and_check(inst, scores=(splits == 0))
     del inst
+    _free()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_small_workload_fused_select_and_attend(name, splits):
+    # sv_select_and_attend: oracle parity, and bit-identical to the separate calls
+    _gpu()
+    PT.log(f"[fused] {name} splits={splits}")
+    w = SMALL[name].with_(num_layers=2, reuse_odd_layers=True)
+    a = Instance(w, seed=12, num_splits=splits, nan_pool=True, fused=True)
+    run_and_check(a)
+    b = Instance(w, seed=12, num_splits=splits, nan_pool=True, fused=False)
+    b.step()
+    torch.cuda.synchronize()
+    for la, lb in zip(a.layers, b.layers):
+        assert torch.equal(la.idx, lb.idx) and torch.equal(la.cnt, lb.cnt)
+        assert torch.equal(la.out, lb.out) and torch.equal(la.lse, lb.lse)
+    del a, b
     _free()
 
 
@@ -219,7 +244,7 @@ def test_stack_with_reuse_small():
 def test_full_llama32k_all_units():
     _gpu()
     PT.log("[full] llama32k")
-    inst = Instance(W["llama32k"], seed=1)
+    inst = Instance(W["llama32k"], seed=1, fused=True)
     run_and_check(inst)
     del inst
     _free()
@@ -228,7 +253,7 @@ def test_full_llama32k_all_units():
 def test_full_ragged_sampled_units():
     _gpu()
     PT.log("[full] ragged")
-    inst = Instance(W["ragged"], seed=2)
+    inst = Instance(W["ragged"], seed=2, fused=True)
     lens = inst.ctx_lens
     bs = [int(np.argmin(lens)), int(np.argmax(lens)), 5, 11]
     units = sorted({(b, g) for b, g in zip(bs, [0, 7, 3, 5])})
@@ -241,7 +266,7 @@ def test_full_ragged_sampled_units():
 def test_full_qwen128k_all_units():
     _gpu()
     PT.log("[full] qwen128k")
-    inst = Instance(W["qwen128k"], seed=4)
+    inst = Instance(W["qwen128k"], seed=4, fused=True)
     run_and_check(inst, check_reps=False)
     del inst
     _free()
@@ -250,7 +275,7 @@ def test_full_qwen128k_all_units():
 def test_full_stack64k_sampled_layers_and_units():
     _gpu()
     PT.log("[full] stack64k (32 layers)")
-    inst = Instance(W["stack64k"], seed=3)
+    inst = Instance(W["stack64k"], seed=3, fused=True)
     run_and_check(inst, units=[(0, 0), (3, 7), (2, 4)], layers=[0, 1, 30, 31], check_reps=False)
     del inst
     _free()
@@ -260,7 +285,7 @@ def test_graph_replays_match_eager():
     # The bench replays a captured pass; every replay must equal the eager pass.
     _gpu()
     w = W["stack64k"].with_(num_seqs=2, num_q_heads=8, num_kv_heads=2, ctx=(8192, 7000))
-    inst = Instance(w, seed=17, num_layers=4)
+    inst = Instance(w, seed=17, num_layers=4, fused=True)
     inst.step()
     torch.cuda.synchronize()
     eager = [(ly.idx.clone(), ly.cnt.clone(), ly.out.clone(), ly.lse.clone()) for ly in inst.layers]
