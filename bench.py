@@ -2,17 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stack64k]
 
-A step is one verification pass over the whole workload: for every layer, block
-selection (sv_select_blocks) or inter-layer reuse (sv_reuse_indices), then sparse
-multi-draft attention (sv_sparse_verify_attn). Inputs are seeded synthetic tensors
-already resident in HBM (the paged KV pools are built with sv_block_repr before
-timing). The step is captured once in a HIP graph and replayed.
+A step is one verification pass over the whole workload: on every selecting layer
+sv_select_and_attend (scoring, budget, top-k, sparse multi-draft attention, merge),
+on every reuse layer sv_sparse_verify_attn over the previous layer's index buffers
+(inter-layer reuse without a copy). Inputs are seeded synthetic tensors already
+resident in HBM (the paged KV pools are built with sv_block_repr before timing). The
+step is captured once in a HIP graph and replayed.
 
 Prints one JSON line. `value` is verified draft-token-heads per second (rows of
 (draft token, query head) per layer, summed over layers and sequences).
-`roofline` refers to the attention entry point (the dominant cost): algorithmic
-bytes (selected K/V of one layer) over its average duration, timed with HIP events
-on the stream it runs on. `cpu_baseline` times the fp64 oracle on a bounded sample of
+`roofline` refers to the attention entry point (the dominant cost; its two kernels,
+attention then merge, run back to back): algorithmic bytes (selected K/V of one
+layer) over its average duration, timed with HIP events on the stream it runs on.
+`traffic` is the HBM traffic per launch from the committed profiler counter summary
+of the attention kernel, reported only while that summary was taken from the
+current kernel source. `cpu_baseline` times the fp64 oracle on a bounded sample of
 the same workload on the host.
 """
 
@@ -30,6 +34,26 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "verify-attn draft-token-heads/s and % HBM peak at 32K-128K ctx, 1 GPU"
+ATTN_SRC = os.path.join(ROOT, "block_sparse_speculative_amd", "csrc", "attn.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "attn_kernel_{workload}_counters.txt")
+
+
+def traffic_from_counters(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, or None when
+    there is none or it was taken from another version of the kernel source."""
+    import hashlib
+    path = COUNTERS.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -43,7 +67,9 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--separate", action="store_true",
+                    help="run the separate-call path (select / reuse copy / attend) instead")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -68,10 +94,10 @@ def copy_calibration(mib: int, reps: int):
 
 
 def cpu_baseline(inst, budget_s: float):
-    """Oracle draft-token-heads/s on host cores, on whole layers of one sequence of the
-    same workload, until about `budget_s` seconds of oracle work. Representatives are
-    computed outside the timed region (they exist before verification)."""
-    import numpy as np
+    """Oracle draft-token-heads/s on host cores over whole layers of the same workload
+    (sequence 0 first, then the next sequences), until about `budget_s` seconds of
+    oracle work. Representatives are computed outside the timed region (they exist
+    before verification), as are the device-to-host copies and the fp64 widening."""
     from threadpoolctl import threadpool_limits
 
     import oracle as O
@@ -79,59 +105,64 @@ def cpu_baseline(inst, budget_s: float):
     w = inst.w
     G, bs, T = w.group, w.block_size, w.num_draft
     dense, mn, frac, kf, kl = w.budget
-    b = 0
-    ctx = inst.ctx_lens[b]
-    timed, rows, layers_done, units_done = 0.0, 0, 0, 0
-    prev = None
+    timed, rows, units_done = 0.0, 0, 0
+    done = []                              # (sequence, layers) covered
     with threadpool_limits(limits=1):
-        for l in range(len(inst.layers)):
-            x = inst.logical(l)
-            q = x["q"][b].float().cpu().numpy()
-            kc = x["k_ctx"][b, :ctx].float().cpu().numpy()
-            vc = x["v_ctx"][b, :ctx].float().cpu().numpy()
-            kd = x["k_draft"][b].float().cpu().numpy()
-            vd = x["v_draft"][b].float().cpu().numpy()
-            del x
-            reuse = inst.layers[l].reuse
-            sels = []
-            for g in range(w.num_kv_heads):
-                sl = slice(g, g + 1)
-                qg = q[:, g * G:(g + 1) * G]
-                if not reuse:
-                    reps = O.block_representatives(kc[:, sl], bs)          # untimed
-                t0 = time.perf_counter()
-                if reuse:
-                    sel = prev[g]
-                else:
-                    sc = O.block_scores(qg[0], reps, G)[0]
-                    k = O.budget_blocks(ctx, bs, dense, mn, frac)
-                    sel = O.select_blocks(sc, k, bool(kf), bool(kl))
-                O.verify_attention(qg, kc[:, sl], vc[:, sl], kd[:, sl], vd[:, sl], [sel], bs,
-                                   inst.scale)
-                timed += time.perf_counter() - t0
-                sels.append(sel)
-                rows += T * G
-                units_done += 1
-            prev = sels
-            layers_done += 1
-            if timed >= budget_s and (not w.reuse_odd_layers or layers_done % 2 == 0):
+        for b in range(w.num_seqs):
+            ctx = inst.ctx_lens[b]
+            prev = None
+            layers_done = 0
+            for l in range(len(inst.layers)):
+                x = inst.logical(l)
+                q = x["q"][b].float().cpu().numpy()
+                kc = x["k_ctx"][b, :ctx].float().cpu().numpy()
+                vc = x["v_ctx"][b, :ctx].float().cpu().numpy()
+                kd = x["k_draft"][b].float().cpu().numpy()
+                vd = x["v_draft"][b].float().cpu().numpy()
+                del x
+                reuse = inst.layers[l].reuse
+                sels = []
+                for g in range(w.num_kv_heads):
+                    sl = slice(g, g + 1)
+                    qg = q[:, g * G:(g + 1) * G]
+                    if not reuse:
+                        reps = O.block_representatives(kc[:, sl], bs)          # untimed
+                    t0 = time.perf_counter()
+                    if reuse:
+                        sel = prev[g]
+                    else:
+                        sc = O.block_scores(qg[0], reps, G)[0]
+                        k = O.budget_blocks(ctx, bs, dense, mn, frac)
+                        sel = O.select_blocks(sc, k, bool(kf), bool(kl))
+                    O.verify_attention(qg, kc[:, sl], vc[:, sl], kd[:, sl], vd[:, sl], [sel],
+                                       bs, inst.scale)
+                    timed += time.perf_counter() - t0
+                    sels.append(sel)
+                    rows += T * G
+                    units_done += 1
+                prev = sels
+                layers_done += 1
+                if timed >= budget_s and (not w.reuse_odd_layers or layers_done % 2 == 0):
+                    break
+            done.append((b, layers_done))
+            if timed >= budget_s:
                 break
+    desc = ", ".join(f"sequence {b} (ctx {inst.ctx_lens[b]}) layers 0..{n - 1}" for b, n in done)
     return {
         "value": rows / timed,
         "unit": "draft-token-heads/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"sequence 0 (ctx {ctx}), layers 0..{layers_done - 1} of {len(inst.layers)}, "
-                   f"all {w.num_kv_heads} KV heads: {units_done} units, {rows} draft-token-heads, "
-                   f"{timed:.1f} s single-threaded numpy fp64 (scores, budget, top-k, attention; "
-                   f"representatives precomputed)"),
+        "sample": (f"{desc} of {len(inst.layers)} layers, all {w.num_kv_heads} KV heads: "
+                   f"{units_done} units, {rows} draft-token-heads, {timed:.1f} s single-threaded "
+                   f"numpy fp64 (scores, budget, top-k, attention; representatives precomputed)"),
     }
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the per-GPU "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the per-GPU "
               f"share of a sharded deployment is the single-GPU workload measured here.",
               file=sys.stderr)
         sys.exit(2)
@@ -161,7 +192,7 @@ def main():
             print(f"[bench]   built layer {done}/{total}", file=sys.stderr, flush=True)
 
     insts = [Instance(w, seed=args.seed + r, num_splits=args.num_splits, with_lse=False,
-                      progress=progress) for r in range(reps_total)]
+                      progress=progress, fused=not args.separate) for r in range(reps_total)]
     inst0 = insts[0]
     torch.cuda.synchronize()
 
@@ -250,6 +281,10 @@ def main():
             "block_size": w.block_size, "draft_tokens": w.num_draft, "k_max": inst0.k_max,
             "reuse": "odd layers reuse" if w.reuse_odd_layers else "none",
             "splits": inst0.num_splits, "graph": use_graph, "resident_instances": reps_total,
+            "path": ("separate calls: sv_select_blocks / sv_reuse_indices, sv_sparse_verify_attn"
+                     if args.separate else
+                     "sv_select_and_attend on selecting layers; sv_sparse_verify_attn on the "
+                     "previous layer's index buffers on reuse layers"),
         },
         "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": bytes_per_pass,
@@ -260,7 +295,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": traffic_from_counters(w.name),
             "avg_launch_us": attn_us,
             "algorithmic_bytes_per_launch": kv_bytes_per_launch,
         },
