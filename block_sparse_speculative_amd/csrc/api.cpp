@@ -4,6 +4,7 @@
 // it enqueues anything.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -126,7 +127,22 @@ size_t select_ws_layout(const sv_shape* s, size_t* scores_off) {
   return align_up(units * s->max_blocks_per_seq * sizeof(float));
 }
 
-// Attention workspace: [partial O][partial (m, l)].
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return sv::kAttnCUs;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = sv::kAttnCUs;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Attention workspace: [merge counters: units x 256 B][partial O][partial (m, l)].
 size_t attn_ws_layout(const sv_shape* s, int splits, size_t* o_off, size_t* ml_off) {
   size_t o_dummy, ml_dummy;
   if (!o_off) o_off = &o_dummy;
@@ -138,8 +154,8 @@ size_t attn_ws_layout(const sv_shape* s, int splits, size_t* o_off, size_t* ml_o
   const size_t rows = static_cast<size_t>(s->num_draft) * (s->num_q_heads / s->num_kv_heads);
   const size_t units = static_cast<size_t>(s->num_seqs) * s->num_kv_heads;
   const size_t parts = static_cast<size_t>(splits) + 1;   // + the draft-only split
-  *o_off = 0;
-  *ml_off = align_up(units * parts * rows * s->head_dim * sizeof(float));
+  *o_off = align_up(units * sv::kTicketStride * sizeof(uint32_t));
+  *ml_off = *o_off + align_up(units * parts * rows * s->head_dim * sizeof(float));
   return *ml_off + align_up(units * parts * rows * 2 * sizeof(float));
 }
 
@@ -209,6 +225,8 @@ sv::AttnParams attn_params(const sv_shape* shape, const void* q, const void* k_d
   p.S = splits;
   p.R = shape->num_draft * p.G;
   p.xcd_group = sv::xcd_groupable(p.B * p.Hkv) ? 1 : 0;
+  p.tickets = ws_need ? reinterpret_cast<uint32_t*>(w) : nullptr;
+  p.merge = sv::attn_merge_mode(splits, p.B * p.Hkv, p.R, shape->dtype == SV_BF16, device_cus());
   p.scale_log2 = scale * 1.44269504088896340736f;
   return p;
 }

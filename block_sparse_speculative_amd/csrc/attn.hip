@@ -42,6 +42,10 @@
 //
 // Merge of the partials of a unit:  O = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
 //  - S == 1: the workgroup normalises and writes the output itself.
+//  - in-kernel (the whole grid resident at once): every workgroup writes its partial
+//    with device-scope stores, takes a device-scope arrival ticket, waits (bounded)
+//    for all workgroups of its unit, then merges its own slice of the unit's rows;
+//    the last of the departure increments clears the ticket.
 //  - otherwise merge_kernel combines the partials in a second launch.
 //
 // XCD placement: workgroups are dispatched to the 8 XCDs round-robin by linear id.
@@ -62,6 +66,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
 
 constexpr float kLn2 = 0.69314718055994530942f;
+// Polls of the sibling wait before a workgroup gives up (and writes NaN): about a
+// second, far beyond any real wait (the siblings are resident and streaming).
+constexpr int kMergeSpinLimit = 1 << 20;
 constexpr int kBtStageMax = 1024;    // block-table rows up to this length are staged in LDS
 static_assert(kWaveTopkMaxBlocks <= kBtStageMax, "the fused select mode reads the staged row");
 
@@ -103,6 +110,86 @@ __device__ __forceinline__ float sum_over_row_lanes(float x) {
   const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false,
                                                   false);
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, untyped); accesses past the
+// end return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// Cache-policy bits of buffer accesses: kDeviceScope (sc1) makes a store or load
+// coherent across the XCDs without a cache writeback fence.
+constexpr int kDeviceScope = 16;
+typedef unsigned int u32x4v __attribute__((__vector_size__(16)));
+typedef unsigned int u32x2v __attribute__((__vector_size__(8)));
+template <int AUX>
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), r, off, 0, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ f32x4 load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, int off, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, v), r, off, 0, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ float2 load2(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+}
+
+// Combines the NP partials of one (unit, row) for the 4 head dims at `dim`:
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, sixteen partials per batch of
+// loads (unconditional, masked afterwards, so a batch is in flight together; a
+// running max rescales across batches). Returns out; *lse2 = M + log2(L).
+template <int AUX>
+__device__ __forceinline__ f32x4 combine_partials(__amdgpu_buffer_rsrc_t po,
+                                                  __amdgpu_buffer_rsrc_t pml, int NP, int R,
+                                                  int D, int row, int dim, float* lse2) {
+  constexpr int BATCH = 16;
+  float mrun = -__builtin_inff(), l = 0.0f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < NP; s0 += BATCH) {
+    float2 ml[BATCH];
+    f32x4 os[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int sk = s0 + k < NP ? s0 + k : NP - 1;
+      ml[k] = load2<AUX>(pml, (sk * R + row) * 8);
+      os[k] = load4<AUX>(po, ((sk * R + row) * D + dim) * 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch issues before any use
+    float mb = mrun;
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k)
+      if (s0 + k < NP) mb = fmaxf(mb, ml[k].x);
+    const float msafe = mb == -__builtin_inff() ? 0.0f : mb;
+    const float a = __builtin_amdgcn_exp2f(mrun - msafe);
+    l *= a;
+    o *= a;
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const float w = s0 + k < NP ? __builtin_amdgcn_exp2f(ml[k].x - msafe) : 0.0f;
+      l += w * ml[k].y;
+      o += w * os[k];
+    }
+    mrun = mb;
+  }
+  *lse2 = mrun + __builtin_log2f(l);
+  return o * (1.0f / l);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out4(void* out, int64_t off, f32x4 v) {
+  if constexpr (BF16) {
+    bf16x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = static_cast<__bf16>(v[e]);
+    *reinterpret_cast<bf16x4_t*>(static_cast<char*>(out) + off * 2) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = v;
+  }
 }
 
 template <bool BF16_, int D_, int TT_, int RP_, int RING_KB_>
@@ -781,23 +868,86 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
     return;
   }
 
-  // Partial of this split: O (unnormalised), running max (log2 units), denominator,
-  // for merge_kernel. With XCD grouping the merge workgroups of the unit run on the
-  // same XCD and find the partials in its L2.
+  // Partial of this split: O (unnormalised), running max (log2 units), denominator.
+  // kMergeKernel: plain stores for merge_kernel (with XCD grouping its workgroups for
+  // the unit run on the same XCD and find them in its L2). kMergeInKernel:
+  // device-scope stores, then every workgroup of the unit waits for its siblings
+  // and merges its own slice of rows.
+  const bool ink = p.merge == kMergeInKernel;
+  const int part_bytes = NP * p.R * D * 4;
+  const __amdgpu_buffer_rsrc_t po =
+      make_rsrc(p.part_o + static_cast<int64_t>(unit) * NP * p.R * D, part_bytes);
+  const __amdgpu_buffer_rsrc_t pml =
+      make_rsrc(p.part_ml + static_cast<int64_t>(unit) * NP * p.R * 2, NP * p.R * 8);
   if (writer) {
-    float* po = p.part_o + static_cast<int64_t>(unit) * NP * p.R * D;
-    float2* pml = reinterpret_cast<float2*>(p.part_ml) + static_cast<int64_t>(unit) * NP * p.R;
 #pragma unroll
     for (int nt = 0; nt < C::NN; ++nt) {
       const int row = row0 + nt * 16 + l16;
       if (row >= p.R) continue;
       const int prow = split * p.R + row;
 #pragma unroll
-      for (int md = 0; md < C::NMD; ++md)
-        *reinterpret_cast<f32x4*>(po + static_cast<int64_t>(prow) * D + md * 16 + 4 * g4) =
-            st.o[md][nt];
-      if (g4 == 0) pml[prow] = make_float2(st.m[nt], st.l[nt]);
+      for (int md = 0; md < C::NMD; ++md) {
+        const int off = (prow * D + md * 16 + 4 * g4) * 4;
+        if (ink) store4<kDeviceScope>(po, off, st.o[md][nt]);
+        else     store4<0>(po, off, st.o[md][nt]);
+      }
+      if (g4 == 0) {
+        const float2 ml = make_float2(st.m[nt], st.l[nt]);
+        if (ink) store2<kDeviceScope>(pml, prow * 8, ml);
+        else     store2<0>(pml, prow * 8, ml);
+      }
     }
+  }
+  if (!ink) return;
+
+  // Arrival: this workgroup's partial has reached the device coherence point before
+  // its ticket is taken; then wait (bounded) until all NP workgroups of the unit have
+  // arrived. The launch only takes this mode when its whole grid is resident at
+  // once, so every sibling is running and the wait ends.
+  wait_vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  lds_barrier();
+  int* flag = reinterpret_cast<int*>(smem + C::FLAG_OFF);
+  if (tid == 0) {
+    uint32_t* ticket = p.tickets + static_cast<int64_t>(unit) * kTicketStride;
+    unsigned v = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    for (int spin = 0; v < static_cast<unsigned>(NP) && spin < kMergeSpinLimit; ++spin) {
+      __builtin_amdgcn_s_sleep(8);
+      v = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *flag = v >= static_cast<unsigned>(NP) ? 1 : 0;
+  }
+  lds_barrier();
+  const bool all_in = *flag != 0;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+  // This workgroup's rows of the unit: [split * rpw, split * rpw + rpw).
+  const int rpw = (p.R + NP - 1) / NP;
+  const int rb = split * rpw;
+  const int re = rb + rpw < p.R ? rb + rpw : p.R;
+  for (int i4 = tid; i4 < (re - rb) * (D / 4); i4 += C::NT) {
+    const int row = rb + i4 / (D / 4);
+    const int dim = (i4 - (row - rb) * (D / 4)) * 4;
+    float lse2;
+    f32x4 v = combine_partials<kDeviceScope>(po, pml, NP, p.R, D, row, dim, &lse2);
+    if (!all_in) {   // a sibling never arrived: make the failure visible
+      v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      lse2 = __builtin_nanf("");
+    }
+    const int t = row / p.G;
+    const int h = g * p.G + (row - t * p.G);
+    const int64_t ob = (static_cast<int64_t>(b) * p.T + t) * p.Hq + h;
+    store_out4<C::BF16>(p.out, ob * D + dim, v);
+    if (p.lse && dim == 0) p.lse[ob] = lse2 * kLn2;
+  }
+
+  // Departure: the last of the unit's 2 * NP ticket increments resets the counter
+  // for the next launch.
+  if (tid == 0) {
+    uint32_t* ticket = p.tickets + static_cast<int64_t>(unit) * kTicketStride;
+    const unsigned d = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == static_cast<unsigned>(2 * NP - 1))
+      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -826,55 +976,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   if (i4 * 4 >= p.R * D) return;
   const int row = (i4 * 4) / D;
   const int dim = i4 * 4 - row * D;
-  const int S = p.S + 1;   // context splits plus the draft split
-  const int64_t base = static_cast<int64_t>(unit) * S * p.R + row;
-  // Loads of a batch are unconditional (an index past the last partial re-reads the
-  // last one) and masked afterwards, so they are all in flight together.
-  constexpr int BATCH = 16;
-  float mrun = -__builtin_inff(), l = 0.0f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += BATCH) {
-    float2 ml[BATCH];
-    f32x4 os[BATCH];
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int sk = s0 + k < S ? s0 + k : S - 1;
-      const int64_t pr = base + static_cast<int64_t>(sk) * p.R;
-      ml[k] = *reinterpret_cast<const float2*>(p.part_ml + pr * 2);
-      os[k] = *reinterpret_cast<const f32x4*>(p.part_o + pr * D + dim);
-    }
-    float mb = mrun;
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k)
-      if (s0 + k < S) mb = fmaxf(mb, ml[k].x);
-    const float msafe = mb == -__builtin_inff() ? 0.0f : mb;
-    const float a = __builtin_amdgcn_exp2f(mrun - msafe);
-    l *= a;
-    o *= a;
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const float w = s0 + k < S ? __builtin_amdgcn_exp2f(ml[k].x - msafe) : 0.0f;
-      l += w * ml[k].y;
-      o += w * os[k];
-    }
-    mrun = mb;
-  }
+  const int NP = p.S + 1;   // context splits plus the draft split
+  const __amdgpu_buffer_rsrc_t po =
+      make_rsrc(p.part_o + static_cast<int64_t>(unit) * NP * p.R * D, NP * p.R * D * 4);
+  const __amdgpu_buffer_rsrc_t pml =
+      make_rsrc(p.part_ml + static_cast<int64_t>(unit) * NP * p.R * 2, NP * p.R * 8);
+  float lse2;
+  const f32x4 v = combine_partials<0>(po, pml, NP, p.R, D, row, dim, &lse2);
   const int b = unit / p.Hkv;
   const int g = unit - b * p.Hkv;
   const int t = row / p.G;
   const int h = g * p.G + (row - t * p.G);
-  const int64_t off = ((static_cast<int64_t>(b) * p.T + t) * p.Hq + h) * D + dim;
-  const f32x4 v = o * (1.0f / l);
-  if constexpr (BF16) {
-    bf16x4_t w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = static_cast<__bf16>(v[e]);
-    *reinterpret_cast<bf16x4_t*>(static_cast<char*>(p.out) + off * 2) = w;
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = v;
-  }
-  if (p.lse && dim == 0)
-    p.lse[(static_cast<int64_t>(b) * p.T + t) * p.Hq + h] = (mrun + __builtin_log2f(l)) * kLn2;
+  const int64_t ob = (static_cast<int64_t>(b) * p.T + t) * p.Hq + h;
+  store_out4<BF16>(p.out, ob * D + dim, v);
+  if (p.lse && dim == 0) p.lse[ob] = lse2 * kLn2;
 }
 
 template <class C>
@@ -918,10 +1033,18 @@ hipError_t launch_dtype(const AttnParams& p, hipStream_t stream) {
 
 }  // namespace
 
+int attn_merge_mode(int splits, int units, int rows, bool bf16, int cus) {
+  if (splits <= 1) return kMergeNone;
+  // workgroups the launch keeps resident per CU: two with the 64 KB ring (bf16), else one
+  const int per_cu = (attn_ring_kb(splits, units, rows, bf16) == 64 && bf16) ? 2 : 1;
+  const int64_t grid = static_cast<int64_t>(splits + 1) * units;
+  return grid <= static_cast<int64_t>(cus) * per_cu ? kMergeInKernel : kMergeKernel;
+}
+
 hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
   hipError_t e = bf16 ? launch_dtype<true>(p, stream) : launch_dtype<false>(p, stream);
-  if (e != hipSuccess || p.S == 1) return e;
+  if (e != hipSuccess || p.merge != kMergeKernel) return e;
   dim3 grid((p.R * p.D / 4 + kMergeThreads - 1) / kMergeThreads * p.B * p.Hkv);
   if (bf16)
     hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(kMergeThreads), 0, stream, p);

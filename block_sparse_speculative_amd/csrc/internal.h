@@ -52,6 +52,8 @@ struct AttnParams {
   float* lse;
   float* part_o;        // [units, S+1, R, D] unnormalised partial outputs
   float* part_ml;       // [units, S+1, R, 2]  (running max in log2 units, denominator)
+  uint32_t* tickets;    // [units][kTicketStride] arrival/departure counters (one per line)
+  int32_t merge;        // kMerge* mode
   int32_t xcd_group;    // nonzero: the workgroups of unit u have linear ids = u mod 8
   int32_t B, Hq, Hkv, G, D, T, bs, NB, P, k_max;
   int32_t S;            // context splits (a draft-only split is added when S > 1)
@@ -79,6 +81,16 @@ hipError_t launch_topk(const SelectParams& p, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_reuse(const ReuseParams& p, hipStream_t stream);
 
+// How the split partials of a unit are combined.
+enum : int32_t {
+  kMergeNone = 0,       // one split: the workgroup writes the output
+  kMergeInKernel = 1,   // the unit's workgroups wait for each other and merge slices
+  kMergeKernel = 2,     // a separate merge_kernel launch
+};
+// Merge mode for a launch: in-kernel when the whole grid is resident at once
+// (cus = compute units of the device).
+int attn_merge_mode(int splits, int units, int rows, bool bf16, int cus);
+
 // Tokens per attention tile (a tile never spans two blocks): 64 for bf16 blocks of
 // 64 or more tokens, else 32.
 inline int attn_tile_tokens(int block_size, bool bf16) {
@@ -86,6 +98,7 @@ inline int attn_tile_tokens(int block_size, bool bf16) {
 }
 
 constexpr int kAttnCUs = 256;        // compute units of the MI355X
+constexpr int kTicketStride = 64;    // uint32 per merge counter: one 256-byte line each
 constexpr int kXcds = 8;             // XCDs; workgroups are dispatched round-robin over them
 
 // Whether the per-unit kernels can place each unit on one XCD.
