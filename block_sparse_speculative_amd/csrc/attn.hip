@@ -303,8 +303,9 @@ __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase
   constexpr int ES = C::ES;
   const int tok0 = grp * 32 + 8 * g4;
   const int vc = (tok0 * ES) >> 4;
-  // Every LDS fragment of the group is requested up front so the reads overlap
-  // each other and the S^T MFMAs.
+  // The group's K fragments are requested together; the V fragments are requested
+  // once the S^T MFMAs are issued (they overlap the MFMAs and the softmax, and reuse
+  // the K fragments' registers).
   uint4 kf[2][C::KFC];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
@@ -312,16 +313,6 @@ __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase
 #pragma unroll
     for (int kc = 0; kc < C::KFC; ++kc)
       kf[mt][kc] = lds_read16(kbase, r * C::NCHK + ((C::KFC * g4 + kc) ^ swz_k<C::NCHK>(r)));
-  }
-  uint4 vf[C::NMD][C::VPM];
-  if constexpr (!DRAFT) {
-#pragma unroll
-    for (int md = 0; md < C::NMD; ++md) {
-      const int r = md * 16 + l16;
-#pragma unroll
-      for (int e = 0; e < C::VPM; ++e)
-        vf[md][e] = lds_read16(vbase, r * C::NCHV + ((vc + e) ^ swz_v<C::NCHV>(r)));
-    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -349,6 +340,17 @@ __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase
       sacc[mt][nt] = acc;
     }
   }
+  uint4 vf[C::NMD][C::VPM];
+  if constexpr (!DRAFT) {
+#pragma unroll
+    for (int md = 0; md < C::NMD; ++md) {
+      const int r = md * 16 + l16;
+#pragma unroll
+      for (int e = 0; e < C::VPM; ++e)
+        vf[md][e] = lds_read16(vbase, r * C::NCHV + ((vc + e) ^ swz_v<C::NCHV>(r)));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- online softmax; the lane holds tokens tok0 + 0..7 of row l16. Scores are
   // raw dot products; c = scale * log2(e) > 0 commutes with the max.

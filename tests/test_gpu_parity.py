@@ -232,6 +232,24 @@ def test_split_counts_agree_within_tolerance():
         assert (o - outs[0]).abs().max().item() <= 1e-2
 
 
+def test_merge_kernel_path_when_the_grid_exceeds_the_device():
+    # 64 units x 17 workgroups > 512 resident workgroups: the separate merge kernel
+    _gpu()
+    w = W["llama32k"].with_(num_seqs=8, ctx=(8192,) * 8)
+    inst = Instance(w, seed=23, num_splits=16, fused=True)
+    assert (inst.num_splits + 1) * 64 > 512
+    run_and_check(inst, units=[(0, 0), (3, 5), (7, 7)])
+
+
+def test_in_kernel_merge_at_full_residency():
+    # 32 units x 16 workgroups = 512 workgroups, two per CU: every one resident
+    _gpu()
+    w = W["stack64k"].with_(num_layers=2, ctx=(8192,) * 4)
+    inst = Instance(w, seed=24, num_splits=15, fused=True)
+    assert (inst.num_splits + 1) * 32 == 512
+    run_and_check(inst, units=[(0, 0), (1, 3), (3, 7)])
+
+
 def test_stack_with_reuse_small():
     _gpu()
     w = W["stack64k"].with_(num_seqs=2, num_q_heads=8, num_kv_heads=2, ctx=(8192, 7000))
