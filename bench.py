@@ -11,9 +11,10 @@ step is captured once in a HIP graph and replayed.
 
 Prints one JSON line. `value` is verified draft-token-heads per second (rows of
 (draft token, query head) per layer, summed over layers and sequences).
-`roofline` refers to the attention entry point (the dominant cost; its two kernels,
-attention then merge, run back to back): algorithmic bytes (selected K/V of one
-layer) over its average duration, timed with HIP events on the stream it runs on.
+`roofline` refers to the attention entry point (the dominant cost; the merge of its
+split partials runs inside the same launch when the grid is resident at once, else
+in a merge kernel right after it): algorithmic bytes (selected K/V of one layer)
+over its average duration, timed with HIP events on the stream it runs on.
 `traffic` is the HBM traffic per launch from the committed profiler counter summary
 of the attention kernel, reported only while that summary was taken from the
 current kernel source. `cpu_baseline` times the fp64 oracle on a bounded sample of
@@ -289,7 +290,8 @@ def main():
         "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": bytes_per_pass,
         "roofline": {
-            "kernel": "sv_sparse_verify_attn (attn_kernel + merge_kernel)",
+            "kernel": "sv_sparse_verify_attn (attn_kernel; split merge inside the launch when "
+                      "the grid is resident, else merge_kernel after it)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
