@@ -17,8 +17,10 @@ in a merge kernel right after it): algorithmic bytes (selected K/V of one layer)
 over its average duration, timed with HIP events on the stream it runs on.
 `traffic` is the HBM traffic per launch from the committed profiler counter summary
 of the attention kernel, reported only while that summary was taken from the
-current kernel source. `cpu_baseline` times the fp64 oracle on a bounded sample of
-the same workload on the host.
+current kernel source. `dense_vs_sparse` times the same attention entry point with
+every block selected at the same context lengths (the dense verification the sparse
+path stands in for). `cpu_baseline` times the fp64 oracle on a bounded sample of the
+same workload on the host.
 """
 
 from __future__ import annotations
@@ -39,8 +41,8 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_speculative_amd", "csrc", "attn.hip"
 COUNTERS = os.path.join(ROOT, "profiles", "attn_kernel_{workload}_counters.txt")
 
 
-def traffic_from_counters(workload: str):
-    """HBM bytes per attention launch from the committed counter summary, or None when
+def counter_field(workload: str, name: str):
+    """A figure of the committed counter summary of the attention kernel, or None when
     there is none or it was taken from another version of the kernel source."""
     import hashlib
     path = COUNTERS.format(workload=workload)
@@ -52,9 +54,9 @@ def traffic_from_counters(workload: str):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("source_sha256") != sha or name not in fields:
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields[name].split()[0])
 
 
 def parse():
@@ -68,6 +70,8 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip timing the dense (every block selected) attention")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--separate", action="store_true",
                     help="run the separate-call path (select / reuse copy / attend) instead")
@@ -157,6 +161,66 @@ def cpu_baseline(inst, budget_s: float):
         "sample": (f"{desc} of {len(inst.layers)} layers, all {w.num_kv_heads} KV heads: "
                    f"{units_done} units, {rows} draft-token-heads, {timed:.1f} s single-threaded "
                    f"numpy fp64 (scores, budget, top-k, attention; representatives precomputed)"),
+    }
+
+
+def dense_vs_sparse(inst, sparse_us: float, reps: int):
+    """The same attention entry point at the same context lengths with every block of
+    every sequence selected (the dense verification the sparse path replaces), on
+    layer 0 of `inst`: its average launch time, its bandwidth over the K/V it reads,
+    and its ratio to the sparse launch time."""
+    import torch
+    from block_sparse_speculative_amd import _lib as L
+    from block_sparse_speculative_amd import pipeline as PL
+
+    w = inst.w
+    B, Hkv = w.num_seqs, w.num_kv_heads
+    nbs = [-(-c // w.block_size) for c in inst.ctx_lens]
+    k_max = max(nbs)
+    idx = torch.full((B, Hkv, k_max), -1, dtype=torch.int32)
+    for b, n in enumerate(nbs):
+        idx[b, :, :n] = torch.arange(n, dtype=torch.int32)
+    idx = idx.to(inst.device)
+    cnt = torch.tensor(nbs, dtype=torch.int32)[:, None].expand(B, Hkv).contiguous().to(inst.device)
+    ws = PL.Workspaces(inst.shape, k_max, 0, inst.device)
+    ly = inst.layers[0]
+    out = torch.empty_like(ly.out)
+
+    def call():
+        L.sparse_verify_attn(inst.shape, ly.q, ly.k_draft, ly.v_draft, ly.pool.k, ly.pool.v,
+                             inst.table, inst.ctx, idx, cnt, k_max, inst.scale, out, ws=ws.attn)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(4):
+            call()
+    stream = torch.cuda.current_stream()
+    graph.replay()
+    stream.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    ev1.record(stream)
+    ev1.synchronize()
+    dense_us = ev0.elapsed_time(ev1) * 1e3 / (4 * reps)
+    elem = 4 if w.dtype == "fp32" else 2
+    dense_bytes = sum(inst.ctx_lens) * Hkv * w.head_dim * 2 * elem
+    return {
+        "ctx": inst.ctx_lens if len(set(inst.ctx_lens)) > 1 else inst.ctx_lens[0],
+        "dense_blocks_per_seq": k_max,
+        "dense_us": dense_us,
+        "sparse_us": sparse_us,
+        "ratio": dense_us / sparse_us,
+        "dense_kv_bytes": dense_bytes,
+        "dense_gbs": dense_bytes / (dense_us * 1e-6) / 1e9,
+        "dense_frac": dense_bytes / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
     }
 
 
@@ -297,11 +361,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic_from_counters(w.name),
+            "traffic": counter_field(w.name, "traffic_bytes_per_launch"),
+            "mfma_busy_pct": counter_field(w.name, "mfma_busy_pct"),
             "avg_launch_us": attn_us,
             "algorithmic_bytes_per_launch": kv_bytes_per_launch,
         },
     }
+    if not args.no_dense:
+        print("[bench] dense verification at the same context", file=sys.stderr, flush=True)
+        result["dense_vs_sparse"] = dense_vs_sparse(inst0, attn_us, max(3, args.steps))
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inst0, args.cpu_seconds)
