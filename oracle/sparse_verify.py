@@ -17,6 +17,9 @@ Sources (cited by short tag below):
   selected set.
 * [SS-ABS]  same page, Abstract: draft tokens are verified in one parallel pass; the
   framework reuses retrieval across draft tokens and across layers.
+* [SPV-TREE] ebiotrade page on SpecPV, Introduction (the EAGLE-3 drafter searches and
+  emits a tree of candidate tokens) and the excerpt on speculative decoding (SpecInfer
+  organises the candidates as a token tree).
 
 Readings taken where the pages leave a step open (each one is listed with its
 justification in the design notes of the repository):
@@ -35,6 +38,9 @@ justification in the design notes of the repository):
 * R9 softmax scale is an argument (1/sqrt(d) by convention).
 * R10 draft token t sees every valid token of the selected blocks plus drafts 0..t.
 * R11 a reuse layer takes the previous layer's selection unchanged.
+* R17 draft trees: draft t has a parent draft (or none: it hangs off the context)
+  that precedes it; draft t sees itself and its ancestors. The chain of R10 is the
+  tree whose parent of t is t - 1. Selection still uses draft 0, the root.
 
 All arithmetic is float64. Inputs may be float32 / bfloat16-valued arrays; they
 are widened to float64 exactly.
@@ -132,25 +138,51 @@ def select_blocks(scores, k: int, keep_first: bool = True, keep_last: bool = Tru
     return np.sort(np.concatenate([np.array(forced, dtype=np.int64), chosen]))
 
 
+def draft_visibility(parents, t_count: int):
+    """The drafts each draft token attends to (readings R10, R17; [SPV-TREE]).
+
+    parents: None for the chain, else a length-T sequence with parents[t] the parent
+    draft of t (-1 for none); a parent must precede its child. Returns a list whose
+    entry t is the ascending array of draft indices draft t sees: t and its ancestors.
+    """
+    if parents is None:
+        return [np.arange(t + 1) for t in range(t_count)]
+    par = [int(x) for x in parents]
+    assert len(par) == t_count
+    vis = []
+    for t in range(t_count):
+        seen = []
+        x = t
+        while x >= 0:
+            assert x <= t and (x == t or x < seen[-1]), "a parent must precede its child"
+            seen.append(x)
+            x = par[x]
+        vis.append(np.array(sorted(seen), dtype=np.int64))
+    return vis
+
+
 def verify_attention(q, k_ctx, v_ctx, k_draft, v_draft, selected, block_size: int,
-                     scale: float):
-    """Multi-draft attention over the shared selected blocks (readings R9, R10;
+                     scale: float, parents=None):
+    """Multi-draft attention over the shared selected blocks (readings R9, R10, R17;
     [SS-F1] shared block set, [SS-ABS] parallel verification of draft tokens).
 
     q:        [T, Hq, D] draft-token queries
     k_ctx:    [ctx, Hkv, D] cached keys (token order), v_ctx likewise
     k_draft:  [T, Hkv, D] keys of the draft tokens themselves, v_draft likewise
     selected: sequence of length Hkv; selected[g] lists logical block indices
+    parents:  None (chain) or the draft tree, as in draft_visibility
     Returns (out [T, Hq, D], lse [T, Hq]) in float64. For draft t and query head
     h of KV head g the key set is every valid token of the blocks in selected[g]
-    followed by drafts 0..t; logits are scale * q.k; out is the softmax-weighted
-    sum of values and lse the natural log of the softmax denominator.
+    followed by the drafts t sees (0..t for the chain, t and its ancestors in a
+    tree); logits are scale * q.k; out is the softmax-weighted sum of values and lse
+    the natural log of the softmax denominator.
     """
     qq = _f64(q)
     t_count, hq, d = qq.shape
     hkv = k_draft.shape[1]
     group = hq // hkv
     ctx = k_ctx.shape[0]
+    vis = draft_visibility(parents, t_count)
     out = np.zeros((t_count, hq, d))
     lse = np.zeros((t_count, hq))
     for g in range(hkv):
@@ -160,8 +192,8 @@ def verify_attention(q, k_ctx, v_ctx, k_draft, v_draft, selected, block_size: in
         kc = _f64(k_ctx[toks, g, :]).reshape(-1, d)
         vc = _f64(v_ctx[toks, g, :]).reshape(-1, d)
         for t in range(t_count):
-            keys = np.concatenate([kc, _f64(k_draft[: t + 1, g, :])], axis=0)
-            vals = np.concatenate([vc, _f64(v_draft[: t + 1, g, :])], axis=0)
+            keys = np.concatenate([kc, _f64(k_draft[vis[t], g, :])], axis=0)
+            vals = np.concatenate([vc, _f64(v_draft[vis[t], g, :])], axis=0)
             for h in range(g * group, (g + 1) * group):
                 z = scale * (keys @ qq[t, h])
                 m = z.max()
@@ -188,13 +220,14 @@ def merge_partials(outs, lses):
 
 
 def verify_layer(q, k_ctx, v_ctx, k_draft, v_draft, ctx_lens, block_size: int,
-                 scale: float, budget, prev_selection=None):
+                 scale: float, budget, prev_selection=None, parents=None):
     """One layer of the verification pass for a batch ([TUT-T1], [SS-F1]).
 
     q [B, T, Hq, D]; k_ctx/v_ctx [B, >=max ctx, Hkv, D]; k_draft/v_draft [B, T, Hkv, D];
     ctx_lens [B]; budget = (dense_ctx_tokens, min_blocks, frac_per_mille,
     keep_first, keep_last). If prev_selection is given (a reuse layer, reading R11)
-    it is used unchanged and no scoring happens.
+    it is used unchanged and no scoring happens. parents: None (chain drafts) or
+    [B][T] draft trees (reading R17).
     Returns dict(out [B,T,Hq,D], lse [B,T,Hq], selection [B][Hkv] arrays,
     scores [B] arrays [Hkv, nb] or None).
     """
@@ -218,7 +251,8 @@ def verify_layer(q, k_ctx, v_ctx, k_draft, v_draft, ctx_lens, block_size: int,
             kb = budget_blocks(ctx, block_size, dense, min_blocks, frac)
             sel = [select_blocks(sc[g], kb, keep_first, keep_last) for g in range(hkv)]
         out[b], lse[b] = verify_attention(q[b], kc, vc, k_draft[b], v_draft[b], sel,
-                                          block_size, scale)
+                                          block_size, scale,
+                                          None if parents is None else parents[b])
         selection.append(sel)
         scores.append(sc)
     return dict(out=out, lse=lse, selection=selection, scores=scores)

@@ -290,6 +290,100 @@ def test_draft_causality():
     assert not np.allclose(base[2], pert[2])          # draft 2 sees itself
 
 
+# ----------------------------------------------------------------- draft trees
+
+
+def _random_tree(rng, T):
+    return [-1] + [int(rng.integers(0, t)) for t in range(1, T)]
+
+
+def _closure_mask(parents):
+    """Ancestor-or-self relation of a draft tree by boolean matrix closure: A[t, u] = 1
+    if u is the parent of t; (I + A)^k for k >= T reaches every ancestor."""
+    T = len(parents)
+    a = np.eye(T, dtype=np.int64)
+    for t, u in enumerate(parents):
+        if u >= 0:
+            a[t, u] = 1
+    r = a.copy()
+    for _ in range(T):
+        r = np.minimum(r @ a, 1)
+    return r.astype(bool)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tree_drafts_equal_sdpa_with_the_ancestor_closure_mask(seed):
+    rng = np.random.default_rng(100 + seed)
+    T = 7
+    p = _problem(seed + 20, T=T)
+    ctx, hkv = p["k_ctx"].shape[:2]
+    parents = _random_tree(rng, T)
+    sel = [np.array([0, 3]), np.array([1, 2, 4])]
+    vis = np.zeros((hkv, ctx), dtype=bool)
+    for g in range(hkv):
+        for j in sel[g]:
+            vis[g, j * p["bs"]: min(ctx, (j + 1) * p["bs"])] = True
+    scale = 0.35
+    out, _ = O.verify_attention(p["q"], p["k_ctx"], p["v_ctx"], p["k_draft"], p["v_draft"],
+                                sel, p["bs"], scale, parents=parents)
+    hq, d = p["q"].shape[1:]
+    g = hq // hkv
+    keys = torch.cat([torch.as_tensor(p["k_ctx"]), torch.as_tensor(p["k_draft"])], 0).double()
+    vals = torch.cat([torch.as_tensor(p["v_ctx"]), torch.as_tensor(p["v_draft"])], 0).double()
+    keys = keys.permute(1, 0, 2).repeat_interleave(g, dim=0)
+    vals = vals.permute(1, 0, 2).repeat_interleave(g, dim=0)
+    mask = torch.zeros((hq, T, ctx + T), dtype=torch.bool)
+    mask[:, :, :ctx] = torch.as_tensor(vis).repeat_interleave(g, dim=0)[:, None, :]
+    mask[:, :, ctx:] = torch.as_tensor(_closure_mask(parents))[None]
+    qq = torch.as_tensor(p["q"]).double().permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qq[None], keys[None], vals[None], attn_mask=mask[None], scale=scale)[0]
+    assert np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_tree_draft_equals_the_chain_of_its_root_path(seed):
+    # Draft t of a tree sees exactly its root path: the chain made of those drafts
+    # alone gives t's row as its last row.
+    rng = np.random.default_rng(200 + seed)
+    T = 8
+    p = _problem(seed + 30, T=T)
+    hkv = p["k_ctx"].shape[1]
+    parents = _random_tree(rng, T)
+    sel = [np.array([1, 2])] * hkv
+    out, lse = O.verify_attention(p["q"], p["k_ctx"], p["v_ctx"], p["k_draft"], p["v_draft"],
+                                  sel, p["bs"], 0.4, parents=parents)
+    for t in range(T):
+        path = [t]
+        while parents[path[-1]] >= 0:
+            path.append(parents[path[-1]])
+        path = path[::-1]
+        o2, l2 = O.verify_attention(p["q"][path], p["k_ctx"], p["v_ctx"], p["k_draft"][path],
+                                    p["v_draft"][path], sel, p["bs"], 0.4)
+        assert np.allclose(out[t], o2[-1], rtol=1e-13, atol=1e-13)
+        assert np.allclose(lse[t], l2[-1], rtol=1e-13, atol=1e-13)
+
+
+def test_chain_tree_is_the_default_and_star_tree_isolates_siblings():
+    p = _problem(40, T=5)
+    hkv = p["k_ctx"].shape[1]
+    sel = [np.array([0, 4])] * hkv
+    args = (p["q"], p["k_ctx"], p["v_ctx"], p["k_draft"], p["v_draft"], sel, p["bs"], 0.5)
+    chain, _ = O.verify_attention(*args)
+    as_tree, _ = O.verify_attention(*args, parents=[-1, 0, 1, 2, 3])
+    assert np.array_equal(chain, as_tree)
+    star, _ = O.verify_attention(*args, parents=[-1, 0, 0, 0, 0])
+    kd, vd = p["k_draft"].copy(), p["v_draft"].copy()
+    kd[2] += 2.0
+    vd[2] -= 3.0
+    pert, _ = O.verify_attention(p["q"], p["k_ctx"], p["v_ctx"], kd, vd, sel, p["bs"], 0.5,
+                                 parents=[-1, 0, 0, 0, 0])
+    assert np.array_equal(star[[0, 1, 3, 4]], pert[[0, 1, 3, 4]])   # siblings of 2 and the root
+    assert not np.allclose(star[2], pert[2])
+    with pytest.raises(AssertionError):
+        O.verify_attention(*args, parents=[-1, 2, 0, 0, 0])        # a parent after its child
+
+
 def test_merge_of_disjoint_subsets_equals_the_whole():
     p = _problem(7, ctx=64, bs=16)
     hkv = 2
