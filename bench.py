@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--separate", action="store_true",
                     help="run the separate-call path (select / reuse copy / attend) instead")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--draft-tree", default="chain", choices=["chain", "random", "star"],
+                    help="draft structure: a chain (the workload's own) or a seeded draft tree")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -140,7 +142,8 @@ def cpu_baseline(inst, budget_s: float):
                         k = O.budget_blocks(ctx, bs, dense, mn, frac)
                         sel = O.select_blocks(sc, k, bool(kf), bool(kl))
                     O.verify_attention(qg, kc[:, sl], vc[:, sl], kd[:, sl], vd[:, sl], [sel],
-                                       bs, inst.scale)
+                                       bs, inst.scale,
+                                       parents=None if inst.parents is None else inst.parents[b])
                     timed += time.perf_counter() - t0
                     sels.append(sel)
                     rows += T * G
@@ -188,7 +191,8 @@ def dense_vs_sparse(inst, sparse_us: float, reps: int):
 
     def call():
         L.sparse_verify_attn(inst.shape, ly.q, ly.k_draft, ly.v_draft, ly.pool.k, ly.pool.v,
-                             inst.table, inst.ctx, idx, cnt, k_max, inst.scale, out, ws=ws.attn)
+                             inst.table, inst.ctx, idx, cnt, k_max, inst.scale, out, ws=ws.attn,
+                             draft_mask=inst.draft_mask)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -245,7 +249,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[args.workload].with_(draft_tree=args.draft_tree)
     # Rotate resident copies so one rotation touches more than 2 x 256 MB of
     # selected data and representatives (the MI355X last-level cache).
     bytes_per_pass = WL.algorithmic_bytes(w, synth.context_lengths(w, args.seed), w.num_layers)
@@ -343,7 +347,8 @@ def main():
             "workload": w.name, "layers": len(inst0.layers), "num_seqs": w.num_seqs,
             "ctx": inst0.ctx_lens if len(set(inst0.ctx_lens)) > 1 else inst0.ctx_lens[0],
             "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-            "block_size": w.block_size, "draft_tokens": w.num_draft, "k_max": inst0.k_max,
+            "block_size": w.block_size, "draft_tokens": w.num_draft,
+            "draft_structure": w.draft_tree, "k_max": inst0.k_max,
             "reuse": "odd layers reuse" if w.reuse_odd_layers else "none",
             "splits": inst0.num_splits, "graph": use_graph, "resident_instances": reps_total,
             "path": ("separate calls: sv_select_blocks / sv_reuse_indices, sv_sparse_verify_attn"

@@ -61,11 +61,11 @@ _SIG = [
                               _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("sv_attn_num_splits", _I, [ctypes.POINTER(Shape), _I, _I]),
     ("sv_attn_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(Shape), _I, _I]),
-    ("sv_sparse_verify_attn", _I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
-                                   ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("sv_sparse_verify_attn", _I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _P, _I, ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     ("sv_select_and_attend_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(Shape), _I, _I]),
     ("sv_select_and_attend", _I, [ctypes.POINTER(Shape), ctypes.POINTER(Budget), _P, _P, _P, _P,
-                                  _P, _P, _P, _P, _I, ctypes.c_float, _I, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, _I, ctypes.c_float, _I, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
     ("sv_reuse_indices", _I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P]),
 ]
@@ -194,8 +194,9 @@ def select_blocks(shape: Shape, budget: Budget, q, repr_pool, block_table, ctx_l
 
 def sparse_verify_attn(shape: Shape, q, k_draft, v_draft, k_pool, v_pool, block_table, ctx_lens,
                        idx, cnt, k_max: int, scale: float, out, lse=None, ws=None,
-                       num_splits: int = 0):
-    """sv_sparse_verify_attn."""
+                       num_splits: int = 0, draft_mask=None):
+    """sv_sparse_verify_attn (draft_mask: None for chain drafts, else [B, T] int32
+    visibility bits among the drafts)."""
     B, Hq, Hkv, D, T = (shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim,
                         shape.num_draft)
     e = _elem(shape)
@@ -214,8 +215,11 @@ def sparse_verify_attn(shape: Shape, q, k_draft, v_draft, k_pool, v_pool, block_
         _dev(lse, "lse", torch.float32, (B, T, Hq))
     if ws is not None:
         _dev(ws, "ws")
+    if draft_mask is not None:
+        _dev(draft_mask, "draft_mask", torch.int32, (B, T))
     _check(lib().sv_sparse_verify_attn(
-        ctypes.byref(shape), _ptr(q), _ptr(k_draft), _ptr(v_draft), _ptr(k_pool), _ptr(v_pool),
+        ctypes.byref(shape), _ptr(q), _ptr(k_draft), _ptr(v_draft), _ptr(draft_mask),
+        _ptr(k_pool), _ptr(v_pool),
         _ptr(block_table), _ptr(ctx_lens), _ptr(idx), _ptr(cnt), int(k_max), float(scale),
         int(num_splits), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()))
@@ -228,7 +232,7 @@ def select_and_attend_workspace_bytes(shape: Shape, k_max: int, num_splits: int 
 
 def select_and_attend(shape: Shape, budget: Budget, q, repr_pool, k_draft, v_draft, k_pool, v_pool,
                       block_table, ctx_lens, k_max: int, scale: float, idx, cnt, out, lse=None,
-                      ws=None, num_splits: int = 0):
+                      ws=None, num_splits: int = 0, draft_mask=None):
     """sv_select_and_attend: selection and attention of one layer; writes idx / cnt."""
     B, Hq, Hkv, D, T = (shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim,
                         shape.num_draft)
@@ -249,9 +253,11 @@ def select_and_attend(shape: Shape, budget: Budget, q, repr_pool, k_draft, v_dra
         _dev(lse, "lse", torch.float32, (B, T, Hq))
     if ws is not None:
         _dev(ws, "ws")
+    if draft_mask is not None:
+        _dev(draft_mask, "draft_mask", torch.int32, (B, T))
     _check(lib().sv_select_and_attend(
         ctypes.byref(shape), ctypes.byref(budget), _ptr(q), _ptr(repr_pool), _ptr(k_draft),
-        _ptr(v_draft), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(ctx_lens), int(k_max),
+        _ptr(v_draft), _ptr(draft_mask), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(ctx_lens), int(k_max),
         float(scale), int(num_splits), _ptr(idx), _ptr(cnt), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()))
 

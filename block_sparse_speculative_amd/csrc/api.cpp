@@ -340,7 +340,8 @@ size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num
 }
 
 sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,
-                                const void* v_draft, const void* k_pool, const void* v_pool,
+                                const void* v_draft, const int32_t* draft_mask,
+                                const void* k_pool, const void* v_pool,
                                 const int32_t* block_table, const int32_t* ctx_lens,
                                 const int32_t* idx, const int32_t* cnt, int32_t k_max,
                                 float scale, int32_t num_splits, void* out, float* lse, void* ws,
@@ -364,6 +365,7 @@ sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void
                                  ctx_lens, k_max, scale, splits, out, lse, ws, need);
   p.idx = idx;
   p.cnt = cnt;
+  p.draft_mask = draft_mask;
   return from_hip(sv::launch_attn(p, shape->dtype == SV_BF16, static_cast<hipStream_t>(stream)),
                   what);
 }
@@ -378,7 +380,7 @@ size_t sv_select_and_attend_workspace_bytes(const sv_shape* shape, int32_t k_max
 
 sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
                                const float* repr_pool, const void* k_draft, const void* v_draft,
-                               const void* k_pool, const void* v_pool,
+                               const int32_t* draft_mask, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* ctx_lens,
                                int32_t k_max, float scale, int32_t num_splits, int32_t* idx,
                                int32_t* cnt, void* out, float* lse, void* ws, size_t ws_bytes,
@@ -413,6 +415,7 @@ sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, c
                                   ctx_lens, k_max, scale, splits, out, lse, ws, attn_need);
   ap.idx = idx;
   ap.cnt = cnt;
+  ap.draft_mask = draft_mask;
   hipError_t e = sv::launch_score(sp, bf16, st);
   if (e != hipSuccess) return from_hip(e, what);
   if (shape->max_blocks_per_seq <= sv::kWaveTopkMaxBlocks) {

@@ -6,7 +6,9 @@
 // Work unit = (sequence b, KV head g). Its rows are the T x G (draft token, query
 // head of the group) pairs, padded to RP in {16, 32, 64, 128}; its keys are the
 // valid tokens of the selected blocks plus the T draft tokens (draft t sees drafts
-// 0..t). Keys are cut into tiles of TT tokens (a tile never spans two blocks). The
+// 0..t of a chain, or itself and its ancestors in a draft tree: SpecPV page,
+// introduction, on tree-shaped candidates). Keys are cut into tiles of TT tokens (a
+// tile never spans two blocks). The
 // k_max * (bs / TT) tile slots of a unit are cut into S balanced contiguous ranges
 // fixed by k_max alone, so a split knows which selected positions it owns before
 // the selected count arrives; slots at or past the count are skipped. One more
@@ -293,13 +295,14 @@ struct WaveState {
 };
 
 // One 32-token group of one tile for one wave. MASKED: tokens >= nvalid (and, for
-// the draft tile, tokens after the row's own draft) are excluded. DRAFT: V is
-// token-major in LDS (the draft tile) instead of dim-major.
+// the draft tile, drafts the row's draft does not see: bit u of tvis) are excluded.
+// DRAFT: V is token-major in LDS (the draft tile) instead of dim-major.
 template <class C, bool MASKED, bool DRAFT>
 __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase,
                                              const char* vbase, int grp, int nvalid,
                                              const uint4 (&qf)[C::NN][C::KFC],
-                                             const int (&trow)[C::NN], float c, int l16, int g4) {
+                                             const uint32_t (&tvis)[C::NN], float c, int l16,
+                                             int g4) {
   constexpr int ES = C::ES;
   const int tok0 = grp * 32 + 8 * g4;
   const int vc = (tok0 * ES) >> 4;
@@ -363,7 +366,7 @@ __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase
       const float x = sacc[jj >> 2][nt][jj & 3];
       if constexpr (MASKED) {
         const int tok = tok0 + jj;
-        const bool vis = tok < nvalid && (!DRAFT || tok <= trow[nt]);
+        const bool vis = tok < nvalid && (!DRAFT || ((tvis[nt] >> (tok & 31)) & 1u));
         s[jj] = vis ? x : -__builtin_inff();
       } else {
         s[jj] = x;
@@ -548,18 +551,23 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
     if (tid < nblk) jv = gidx[tid];
   }
 
-  // Row r of this wave's N-tile nt: (draft t, head hl) = (row / G, row % G).
+  // Row r of this wave's N-tile nt: (draft t, head hl) = (row / G, row % G). tvis:
+  // the drafts draft t sees, as bits: 0..t (a chain), or the caller's draft_mask row
+  // (a tree: t's ancestors), t itself always. Padding rows see every draft.
   const int row0 = rg * C::RW;
   uint4 qf[C::NN][C::KFC];
-  int trow[C::NN];
+  uint32_t tvis[C::NN];
   {
     const char* qbase = static_cast<const char*>(p.q);
 #pragma unroll
     for (int nt = 0; nt < C::NN; ++nt) {
       const int row = row0 + nt * 16 + l16;
       const int t = row / p.G;
-      trow[nt] = t;
       const bool ok = row < p.R;
+      if (p.draft_mask)
+        tvis[nt] = ok ? (static_cast<uint32_t>(p.draft_mask[b * p.T + t]) | (1u << t)) : ~0u;
+      else
+        tvis[nt] = ok ? (2u << t) - 1u : ~0u;
       const int h = g * p.G + (row - t * p.G);
       const char* src = qbase + ((static_cast<int64_t>(b) * p.T + t) * p.Hq + h) * D * ES;
 #pragma unroll
@@ -765,7 +773,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
 #pragma unroll 1
       for (int grp = tg; grp < C::NGRP; grp += C::NTG) {
         if (grp * 32 >= p.T) break;
-        attend_group<C, true, true>(st, kbase, vbase, grp, p.T, qf, trow, c, l16, g4);
+        attend_group<C, true, true>(st, kbase, vbase, grp, p.T, qf, tvis, c, l16, g4);
       }
       continue;
     }
@@ -774,14 +782,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
     if (nvalid == TT) {
 #pragma unroll 1
       for (int grp = tg; grp < C::NGRP; grp += C::NTG)
-        attend_group<C, false, false>(st, kbase, vbase, grp, TT, qf, trow, c, l16, g4);
+        attend_group<C, false, false>(st, kbase, vbase, grp, TT, qf, tvis, c, l16, g4);
     } else if (nvalid > 0) {
       zero_tail(buf, nvalid);
       lds_barrier();
 #pragma unroll 1
       for (int grp = tg; grp < C::NGRP; grp += C::NTG) {
         if (grp * 32 >= nvalid) break;
-        attend_group<C, true, false>(st, kbase, vbase, grp, nvalid, qf, trow, c, l16, g4);
+        attend_group<C, true, false>(st, kbase, vbase, grp, nvalid, qf, tvis, c, l16, g4);
       }
     }
   }

@@ -39,6 +39,7 @@ struct AttnParams {
   const void* q;
   const void* k_draft;
   const void* v_draft;
+  const int32_t* draft_mask;   // [B][T] visibility bits among the drafts, or null (chain)
   const void* k_pool;
   const void* v_pool;
   const int32_t* block_table;

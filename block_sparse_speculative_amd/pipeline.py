@@ -78,13 +78,14 @@ def select(shape, budget, q, pool: Pool, block_table, ctx_lens, k_max, idx, cnt,
 
 
 def select_and_attend(shape, budget, q, k_draft, v_draft, pool: Pool, block_table, ctx_lens,
-                      k_max, scale, idx, cnt, out, ws: Workspaces, lse=None):
+                      k_max, scale, idx, cnt, out, ws: Workspaces, lse=None, draft_mask=None):
     L.select_and_attend(shape, budget, q, pool.reps, k_draft, v_draft, pool.k, pool.v,
                         block_table, ctx_lens, k_max, scale, idx, cnt, out, lse=lse,
-                        ws=ws.fused, num_splits=ws.num_splits)
+                        ws=ws.fused, num_splits=ws.num_splits, draft_mask=draft_mask)
 
 
 def attend(shape, q, k_draft, v_draft, pool: Pool, block_table, ctx_lens, idx, cnt, k_max, scale,
-           out, ws: Workspaces, lse=None):
+           out, ws: Workspaces, lse=None, draft_mask=None):
     L.sparse_verify_attn(shape, q, k_draft, v_draft, pool.k, pool.v, block_table, ctx_lens, idx,
-                         cnt, k_max, scale, out, lse=lse, ws=ws.attn, num_splits=ws.num_splits)
+                         cnt, k_max, scale, out, lse=lse, ws=ws.attn, num_splits=ws.num_splits,
+                         draft_mask=draft_mask)

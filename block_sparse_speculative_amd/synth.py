@@ -24,6 +24,10 @@ seeded Gaussian data):
 
 q_hat of KV head g is the unit vector along the sum of the first draft token's
 queries of the heads in that GQA group (computed from the rounded queries).
+
+Draft trees (any workload, draft_tree != "chain"): draft 0 is the root; in a
+"random" tree the parent of draft t >= 1 is uniform over drafts 0..t-1, drawn per
+sequence; in a "star" every draft t >= 1 hangs off the root.
 """
 
 from __future__ import annotations
@@ -56,6 +60,7 @@ class Workload:
     paged: bool                    # random physical block table
     reuse_odd_layers: bool
     pair_overlap: float = 0.8
+    draft_tree: str = "chain"      # "chain" | "random" | "star"
 
     @property
     def group(self) -> int:
@@ -225,3 +230,36 @@ def make_layer(w: Workload, seed: int, layer: int = 0, device="cpu", ctx_lens=No
 
 def softmax_scale(w: Workload) -> float:
     return 1.0 / math.sqrt(w.head_dim)
+
+
+def draft_parents(w: Workload, seed: int):
+    """Parent draft of every draft token, per sequence ([B][T], -1 for the root), or
+    None for chain drafts."""
+    if w.draft_tree == "chain":
+        return None
+    T = w.num_draft
+    if w.draft_tree == "star":
+        return [[-1] + [0] * (T - 1) for _ in range(w.num_seqs)]
+    if w.draft_tree != "random":
+        raise ValueError(f"unknown draft tree {w.draft_tree!r}")
+    g = _gen(seed, 7_000_001, "cpu")
+    out = []
+    for _ in range(w.num_seqs):
+        par = [-1]
+        for t in range(1, T):
+            par.append(int(torch.randint(0, t, (1,), generator=g).item()))
+        out.append(par)
+    return out
+
+
+def draft_mask(parents, num_draft: int) -> torch.Tensor:
+    """The drafts each draft sees, as bits (int32 [B, T]): itself and its ancestors."""
+    m = torch.zeros((len(parents), num_draft), dtype=torch.int32)
+    for b, par in enumerate(parents):
+        for t in range(num_draft):
+            bits, x = 0, t
+            while x >= 0:
+                bits |= 1 << x
+                x = par[x]
+            m[b, t] = bits
+    return m

@@ -60,6 +60,10 @@ class Instance:
         self.ws = PL.Workspaces(self.shape, self.k_max, num_splits, self.device)
         self.num_splits = L.attn_num_splits(self.shape, self.k_max, num_splits)
         self.fused = fused
+        # Draft tree (None: chain drafts) and its visibility bits on the device.
+        self.parents = synth.draft_parents(w, seed)
+        self.draft_mask = (None if self.parents is None else
+                           synth.draft_mask(self.parents, w.num_draft).to(self.device))
         n_layers = w.num_layers if num_layers is None else num_layers
         B, T, Hq, Hkv, D = w.num_seqs, w.num_draft, w.num_q_heads, w.num_kv_heads, w.head_dim
         self.layers: List[Layer] = []
@@ -100,7 +104,8 @@ class Instance:
     def attend(self, l: int):
         ly = self.layers[l]
         PL.attend(self.shape, ly.q, ly.k_draft, ly.v_draft, ly.pool, self.table, self.ctx, ly.idx,
-                  ly.cnt, self.k_max, self.scale, ly.out, self.ws, lse=ly.lse)
+                  ly.cnt, self.k_max, self.scale, ly.out, self.ws, lse=ly.lse,
+                  draft_mask=self.draft_mask)
 
     def run_layer(self, l: int):
         ly = self.layers[l]
@@ -112,7 +117,7 @@ class Instance:
         else:
             PL.select_and_attend(self.shape, self.budget, ly.q, ly.k_draft, ly.v_draft, ly.pool,
                                  self.table, self.ctx, self.k_max, self.scale, ly.idx, ly.cnt,
-                                 ly.out, self.ws, lse=ly.lse)
+                                 ly.out, self.ws, lse=ly.lse, draft_mask=self.draft_mask)
 
     def step(self):
         for l in range(len(self.layers)):

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 1
+#define SV_ABI_VERSION 2
 
 typedef enum sv_status {
   SV_OK = 0,
@@ -166,12 +166,18 @@ size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num
  * draft tokens are verified in one parallel pass).
  *
  * Draft token t of query head h (KV head g = h / G) attends over every valid
- * context token of the blocks idx[b, g, 0:cnt[b,g]] and over draft tokens 0..t:
+ * context token of the blocks idx[b, g, 0:cnt[b,g]] and over the draft tokens it
+ * sees: drafts 0..t (a chain) when draft_mask is NULL, else every draft u whose bit
+ * draft_mask[b, t] >> u & 1 is set, and always t itself. A draft tree (SpecPV page,
+ * introduction: the EAGLE-3 drafter emits a tree of candidate tokens) is given by
+ * setting the bits of t's ancestors (tree attention):
  *   out[b,t,h,:] = softmax_k(scale * q[b,t,h,:] . key_k) @ value_k
  *   lse[b,t,h]   = natural log of the softmax denominator (of the scaled logits)
  * Accumulation is float32; `out` is rounded to dtype (round to nearest even).
  *   q                 [B, T, Hq, D]   dtype
  *   k_draft, v_draft  [B, T, Hkv, D]  dtype (the draft tokens' own keys/values)
+ *   draft_mask        [B, T] int32 (device) or NULL: visibility bits among the drafts;
+ *                     bits at or above T are ignored
  *   k_pool, v_pool, block_table      as above
  *   ctx_lens [B] int32; idx [B, Hkv, k_max]; cnt [B, Hkv]   (device)
  *   out [B, T, Hq, D] dtype; lse [B, T, Hq] float32 or NULL
@@ -185,7 +191,8 @@ size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num
  * Calls that may run concurrently must not share a workspace. scale must be finite
  * and > 0. */
 sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,
-                                const void* v_draft, const void* k_pool, const void* v_pool,
+                                const void* v_draft, const int32_t* draft_mask,
+                                const void* k_pool, const void* v_pool,
                                 const int32_t* block_table, const int32_t* ctx_lens,
                                 const int32_t* idx, const int32_t* cnt, int32_t k_max,
                                 float scale, int32_t num_splits, void* out, float* lse,
@@ -214,7 +221,7 @@ size_t sv_select_and_attend_workspace_bytes(const sv_shape* shape, int32_t k_max
  *                    Calls that may run concurrently must not share it. */
 sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
                                const float* repr_pool, const void* k_draft, const void* v_draft,
-                               const void* k_pool, const void* v_pool,
+                               const int32_t* draft_mask, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* ctx_lens,
                                int32_t k_max, float scale, int32_t num_splits, int32_t* idx,
                                int32_t* cnt, void* out, float* lse, void* ws, size_t ws_bytes,

@@ -11,6 +11,7 @@ from .sparse_verify import (  # noqa: F401
     budget_blocks,
     block_scores,
     select_blocks,
+    draft_visibility,
     verify_attention,
     merge_partials,
     verify_layer,

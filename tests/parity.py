@@ -86,11 +86,12 @@ def check_selection(gpu_sel, oracle_sel, scores, k, nb, keep_first, keep_last):
     return "near-tie"
 
 
-def check_output(gpu_out, gpu_lse, u: UnitInputs, sel, bs: int, scale: float, dtype: str):
+def check_output(gpu_out, gpu_lse, u: UnitInputs, sel, bs: int, scale: float, dtype: str,
+                 parents=None):
     """Compare one unit's GPU output [T, G, D] (and lse [T, G]) with the oracle run on
-    the same selection. Returns (max_abs, mean_abs)."""
+    the same selection (and draft tree). Returns (max_abs, mean_abs)."""
     ref, ref_lse = O.verify_attention(u.q, u.k_ctx, u.v_ctx, u.k_draft, u.v_draft, [sel], bs,
-                                      scale)
+                                      scale, parents=parents)
     err = np.abs(gpu_out - ref)
     tol = TOL[dtype]
     assert np.isfinite(gpu_out).all(), "non-finite output"
@@ -161,7 +162,8 @@ def verify_instance_units(inst, layer: int, units, logical=None, prev_sel=None, 
                            u, bs, reps)
         gout = out[b, :, g * G:(g + 1) * G]
         glse = None if lse is None else lse[b, :, g * G:(g + 1) * G]
-        mx, _ = check_output(gout, glse, u, used, bs, inst.scale, w.dtype)
+        par = None if inst.parents is None else inst.parents[b]
+        mx, _ = check_output(gout, glse, u, used, bs, inst.scale, w.dtype, parents=par)
         stats["max_abs"] = max(stats["max_abs"], mx)
         sels[(b, g)] = used
     return sels, stats

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = sv.lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert sv.abi_version() == 1
+    assert sv.abi_version() == 2
 
 
 def test_status_strings():
@@ -79,9 +79,9 @@ def _shape(**kw):
 
 def _attn(shape, k_max=64, ws=None, ws_bytes=0, out=FAKE, scale=0.1, splits=0):
     lib = sv.lib()
-    return lib.sv_sparse_verify_attn(ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                     FAKE, FAKE, k_max, scale, splits, out, None, ws, ws_bytes,
-                                     None)
+    return lib.sv_sparse_verify_attn(ctypes.byref(shape), FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, FAKE, k_max, scale, splits, out, None, ws,
+                                     ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -176,9 +176,9 @@ def test_select_and_attend_rejects_before_launch():
     assert need >= sv.attn_workspace_bytes(shape, 64) + 2 * 8 * 1024 * 4
 
     def call(budget=good, ws=FAKE, ws_bytes=need, k_max=64, scale=0.1, q=FAKE, splits=0):
-        return lib.sv_select_and_attend(ctypes.byref(shape), budget, q, FAKE, FAKE, FAKE, FAKE,
-                                        FAKE, FAKE, FAKE, k_max, scale, splits, FAKE, FAKE, FAKE,
-                                        None, ws, ws_bytes, None)
+        return lib.sv_select_and_attend(ctypes.byref(shape), budget, q, FAKE, FAKE, FAKE, None,
+                                        FAKE, FAKE, FAKE, FAKE, k_max, scale, splits, FAKE, FAKE,
+                                        FAKE, None, ws, ws_bytes, None)
 
     assert call(budget=None) == 1
     assert call(budget=ctypes.byref(sv.make_budget(4096, 1, 50, 1, 1))) == 2
@@ -189,8 +189,8 @@ def test_select_and_attend_rejects_before_launch():
     assert call(scale=0.0) == 2
     assert call(splits=-1) == 2
     assert lib.sv_select_and_attend(ctypes.byref(_shape(head_dim=96)), good, FAKE, FAKE, FAKE,
-                                    FAKE, FAKE, FAKE, FAKE, FAKE, 64, 0.1, 0, FAKE, FAKE, FAKE,
-                                    None, FAKE, need, None) == 3
+                                    FAKE, None, FAKE, FAKE, FAKE, FAKE, 64, 0.1, 0, FAKE, FAKE,
+                                    FAKE, None, FAKE, need, None) == 3
 
 
 def test_split_ranges_balanced_over_k_max():

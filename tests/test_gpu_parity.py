@@ -176,6 +176,66 @@ def test_k_max_larger_than_budget_pads_with_minus_one():
     assert cnt[0].tolist() == [16, 16] and cnt[1].tolist() == [5, 5]
 
 
+# ------------------------------------------------------------------ draft trees
+
+TREES = {
+    "llama_small": SMALL["llama_small"],
+    "qwen_small": SMALL["qwen_small"],                  # T = 16: all 16 mask bits in use
+    "fp32_rows32_bs128": SMALL["fp32_rows32_bs128"],
+    "edge": EDGE,                                       # ctx 0: the drafts alone
+}
+
+
+@pytest.mark.parametrize("tree", ["random", "star"])
+@pytest.mark.parametrize("name", list(TREES))
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_draft_tree_all_units(name, tree, splits):
+    # tree attention among the drafts: oracle parity on every unit, and the fused and
+    # separate entry points bit-identical
+    _gpu()
+    PT.log(f"[tree] {name} {tree} splits={splits}")
+    w = TREES[name].with_(draft_tree=tree, num_layers=2, reuse_odd_layers=True)
+    a = Instance(w, seed=31, num_splits=splits, nan_pool=True, fused=True)
+    assert a.draft_mask is not None
+    run_and_check(a)
+    b = Instance(w, seed=31, num_splits=splits, nan_pool=True, fused=False)
+    b.step()
+    torch.cuda.synchronize()
+    for la, lb in zip(a.layers, b.layers):
+        assert torch.equal(la.out, lb.out) and torch.equal(la.lse, lb.lse)
+    del a, b
+    _free()
+
+
+def test_chain_mask_self_bit_and_high_bits():
+    # the chain's bits give exactly the mask-free result; a draft always sees itself;
+    # bits at or above T are ignored
+    _gpu()
+    w = SMALL["llama_small"]
+    T, B = w.num_draft, w.num_seqs
+    ref = _outputs(Instance(w, seed=32))
+    chain = [[t - 1 for t in range(T)]] * B
+    full = synth.draft_mask(chain, T)
+    variants = [full, full & ~torch.tensor([1 << t for t in range(T)], dtype=torch.int32),
+                full | (1 << T) | (1 << 30)]
+    for m in variants:
+        inst = Instance(w, seed=32)
+        inst.draft_mask = m.to(inst.device)
+        for x, y in zip(_outputs(inst), ref):
+            assert torch.equal(x, y)
+
+
+def test_full_stack64k_tree_sampled_units():
+    # the bench shape with a random draft tree, in the library's launch configuration
+    _gpu()
+    PT.log("[full] stack64k random tree")
+    w = W["stack64k"].with_(num_layers=2, draft_tree="random")
+    inst = Instance(w, seed=33, fused=True)
+    run_and_check(inst, units=[(0, 0), (1, 3), (2, 6), (3, 7)])
+    del inst
+    _free()
+
+
 # ------------------------------------------------------------------ invariances
 
 def _outputs(inst):

@@ -444,3 +444,24 @@ def test_planted_blocks_are_recovered_on_the_tiny_workload():
         assert len(sel) == 16 and sel == sorted(sel)
         assert sel[0] == 0 and sel[-1] == nb - 1
         assert set(x["heavy"][0][g]) <= set(sel)
+
+
+@pytest.mark.parametrize("tree", ["chain", "star", "random"])
+def test_input_tree_masks_agree_with_the_oracle_visibility(tree):
+    # The visibility bits the GPU path receives (built by the input module) and the
+    # oracle's own walk over the parents must describe the same draft sets.
+    from block_sparse_speculative_amd import synth
+    w = synth.WORKLOADS["stack64k"].with_(draft_tree=tree, num_seqs=6)
+    parents = synth.draft_parents(w, seed=3)
+    if tree == "chain":
+        assert parents is None
+        parents = [[t - 1 for t in range(w.num_draft)]] * w.num_seqs
+    mask = synth.draft_mask(parents, w.num_draft)
+    for b in range(w.num_seqs):
+        assert all(parents[b][t] < t for t in range(w.num_draft))
+        vis = O.draft_visibility(parents[b], w.num_draft)
+        for t in range(w.num_draft):
+            bits = int(mask[b, t])
+            assert sorted(u for u in range(w.num_draft) if bits >> u & 1) == vis[t].tolist()
+    if tree == "random":
+        assert len({tuple(p) for p in parents}) > 1     # drawn per sequence
