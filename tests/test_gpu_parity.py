@@ -236,6 +236,72 @@ def test_full_stack64k_tree_sampled_units():
     _free()
 
 
+# ------------------------------------------------------------------ full verification and
+# the decode-loop append
+
+def test_full_verification_dense_at_64k_sampled_units():
+    # Periodic full verification runs through the same entry points with a budget that
+    # keeps every block: 1024 blocks per unit at the stack64k shape, then a reuse layer.
+    _gpu()
+    PT.log("[full] stack64k dense verification")
+    w = W["stack64k"].with_(num_layers=2, budget=(1 << 30, 64, 50, 1, 1))
+    inst = Instance(w, seed=34, fused=True)
+    assert inst.k_max == 1024
+    run_and_check(inst, units=[(0, 0), (3, 7)], check_reps=False)
+    cnt = inst.layers[1].cnt.cpu()
+    assert (cnt == 1024).all()
+    del inst
+    _free()
+
+
+def test_decode_loop_append_matches_bulk_bit_identical():
+    # Accepted tokens (1..T per sequence and step, different per sequence) appended
+    # after each verification pass leave the pool and the representatives exactly as a
+    # bulk append of the final contexts would.
+    _gpu()
+    from block_sparse_speculative_amd import pipeline as PL
+    w = SMALL["ragged_small"]
+    final = Instance(w, seed=35, num_layers=1)
+    lens = final.ctx_lens
+    x = final.logical(0)
+    shape, table = final.shape, final.table
+    B, T = w.num_seqs, w.num_draft
+    pool = PL.alloc_pool(shape, final.device, fill_nan=True)
+    start = [max(0, c - 300) for c in lens]
+    PL.append(shape, pool, x["k_ctx"][:, :max(start)].contiguous(),
+              x["v_ctx"][:, :max(start)].contiguous(),
+              torch.tensor(start, dtype=torch.int32, device=final.device),
+              torch.zeros(B, dtype=torch.int32, device=final.device), table)
+    cur = list(start)
+    g = torch.Generator().manual_seed(36)
+    while any(c < l for c, l in zip(cur, lens)):
+        acc = [min(int(torch.randint(1, T + 1, (1,), generator=g)), l - c) for c, l in zip(cur, lens)]
+        n_max = max(max(acc), 1)
+        kn = torch.zeros((B, n_max) + tuple(x["k_ctx"].shape[2:]), dtype=x["k_ctx"].dtype,
+                         device=final.device)
+        vn = torch.zeros_like(kn)
+        for b in range(B):
+            kn[b, :acc[b]] = x["k_ctx"][b, cur[b]:cur[b] + acc[b]]
+            vn[b, :acc[b]] = x["v_ctx"][b, cur[b]:cur[b] + acc[b]]
+        PL.append(shape, pool, kn, vn, torch.tensor(acc, dtype=torch.int32, device=final.device),
+                  torch.tensor(cur, dtype=torch.int32, device=final.device), table)
+        cur = [c + a for c, a in zip(cur, acc)]
+    torch.cuda.synchronize()
+    ref = final.layers[0].pool
+    for b, c in enumerate(lens):
+        nb = -(-c // w.block_size)
+        phys = final.table_host[b, :nb].to(final.device).long()
+        assert torch.equal(pool.reps[phys], ref.reps[phys])
+        full = c // w.block_size
+        assert torch.equal(pool.k[phys[:full]], ref.k[phys[:full]])
+        assert torch.equal(pool.v[phys[:full]], ref.v[phys[:full]])
+        tail = c - full * w.block_size
+        if tail:
+            last = phys[full]
+            assert torch.equal(pool.k[last][:, :tail], ref.k[last][:, :tail])
+            assert torch.equal(pool.v[last][:, :, :tail], ref.v[last][:, :, :tail])
+
+
 # ------------------------------------------------------------------ invariances
 
 def _outputs(inst):
