@@ -18,9 +18,10 @@
 // Prologue: the block-table row, the split's block indices (or, in the fused
 // select mode, the unit's block scores), the context length and the query
 // fragments are requested together, so one round trip precedes the first tile.
-// In the fused select mode one wavefront of every context split runs the exact
-// budget + top-k of the unit from the scores (topk_wave.h) and keeps the positions
-// its split owns; split 0 also writes the unit's indices and count.
+// In the fused select mode every context-split workgroup runs the exact budget +
+// top-k of the unit from the scores (topk_wg.h: the keys spread over all its
+// wavefronts) and keeps the positions its split owns; split 0 also writes the unit's
+// indices and count.
 //
 // Data movement: tiles stream HBM -> LDS through 16-byte LDS-DMA loads
 // (global_load_lds_dwordx4) into a ring of NBUF buffers, so NBUF - 1 tiles are in
@@ -57,7 +58,7 @@
 // handoff between kernels then costs no memory round trip). This is placement for
 // speed only; kernel boundaries keep the results coherent wherever a workgroup runs.
 #include "internal.h"
-#include "topk_wave.h"
+#include "topk_wg.h"
 
 namespace sv {
 namespace {

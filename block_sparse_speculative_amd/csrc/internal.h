@@ -119,8 +119,9 @@ inline int attn_padded_rows(int rows) {
 }
 
 constexpr int kSelectChunk = 128;     // blocks scored by one select workgroup
-// Longest block-table row whose top-k one wavefront does in registers (the fused
-// select-and-attend mode needs it; longer rows take the separate top-k kernel).
+// Longest block-table row whose top-k one workgroup does with its keys in registers
+// (the fused select-and-attend mode needs it; longer rows take the separate LDS
+// top-k kernel).
 constexpr int kWaveTopkMaxBlocks = 1024;
 // Most selected blocks one attention split stages descriptors for (the split count
 // is raised so that no split covers more).

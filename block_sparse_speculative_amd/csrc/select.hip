@@ -14,11 +14,11 @@
 //  top-k         grid = (Hkv, B): budget, then
 //                 - NB <= 1024: the keys spread over the registers of four
 //                   wavefronts, LDS radix select with a single-register finish and
-//                   ballot compaction (topk_wave.h);
+//                   ballot compaction (topk_wg.h);
 //                 - larger NB: an LDS radix select on the same order-preserving
 //                   keys and an ascending compaction with block-wide scans.
 #include "internal.h"
-#include "topk_wave.h"
+#include "topk_wg.h"
 
 namespace sv {
 namespace {
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
 
 // One workgroup of kTopkWaves wavefronts per unit (NB <= 1024).
 constexpr int kTopkWaves = 4;
-__global__ __launch_bounds__(kTopkWaves * 64) void topk_wave_kernel(SelectParams p) {
+__global__ __launch_bounds__(kTopkWaves * 64) void topk_wg_kernel(SelectParams p) {
   const int tid = threadIdx.x;
   const int g = blockIdx.x;
   const int b = blockIdx.y;
@@ -307,9 +307,9 @@ hipError_t launch_score(const SelectParams& p, bool bf16, hipStream_t stream) {
 
 hipError_t launch_topk(const SelectParams& p, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
-  static_assert(kWaveTopkMax == kWaveTopkMaxBlocks, "one wave holds a whole row");
+  static_assert(kWaveTopkMax == kWaveTopkMaxBlocks, "one workgroup holds a whole row");
   if (p.NB <= kWaveTopkMax) {
-    hipLaunchKernelGGL(topk_wave_kernel, dim3(p.Hkv, p.B), dim3(kTopkWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL(topk_wg_kernel, dim3(p.Hkv, p.B), dim3(kTopkWaves * 64), 0, stream, p);
   } else {
     const size_t lds = static_cast<size_t>(p.NB) * sizeof(uint32_t);
     hipLaunchKernelGGL(topk_kernel, dim3(p.Hkv, p.B), dim3(NT), lds, stream, p);

@@ -209,10 +209,11 @@ size_t sv_select_and_attend_workspace_bytes(const sv_shape* shape, int32_t k_max
  * caption: the first draft token's query picks the blocks that all drafts share).
  *
  * Launches: the scoring kernel, then the attention kernel, whose context workgroups
- * each run the budget + top-k of their unit from the scores (one wavefront, exact,
- * lowest index wins ties) before streaming their share of the selected blocks;
- * split 0 of each unit writes idx / cnt. With NB > 1024 the separate top-k kernel
- * runs between the two instead. Then the merge kernel when the splits need one.
+ * each run the budget + top-k of their unit from the scores (exact, lowest index
+ * wins ties) before streaming their share of the selected blocks; split 0 of each
+ * unit writes idx / cnt. With NB > 1024 the separate top-k kernel runs between the
+ * two instead. The split partials are merged inside the attention launch when its
+ * grid is resident at once, else by a merge kernel after it.
  *   arguments        as in sv_select_blocks and sv_sparse_verify_attn
  *   idx, cnt         outputs (as sv_select_blocks writes them)
  *   ws               sv_select_and_attend_workspace_bytes() bytes: the attention
