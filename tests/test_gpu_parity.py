@@ -183,6 +183,7 @@ TREES = {
     "qwen_small": SMALL["qwen_small"],                  # T = 16: all 16 mask bits in use
     "fp32_rows32_bs128": SMALL["fp32_rows32_bs128"],
     "edge": EDGE,                                       # ctx 0: the drafts alone
+    "long_table": SMALL["long_table"],                  # > 1024 blocks: separate top-k
 }
 
 
