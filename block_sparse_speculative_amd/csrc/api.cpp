@@ -100,7 +100,8 @@ sv_status check_kmax(const sv_shape* s, int32_t k_max, const char* what) {
 // each needs a CU: 128 padded rows or fp32), but no fewer than about four tiles per
 // split, so the per-workgroup prologue and the merge stay small next to the stream.
 int resolve_splits(const sv_shape* s, int32_t k_max, int32_t num_splits) {
-  const int tt = sv::attn_tile_tokens(s->block_size, s->dtype == SV_BF16);
+  const int tt = sv::attn_tile_tokens(s->block_size, s->dtype == SV_BF16,
+                                     s->num_draft * (s->num_q_heads / s->num_kv_heads));
   const int64_t ctx_tiles = static_cast<int64_t>(k_max) * (s->block_size / tt);
   int64_t want = num_splits;
   if (want <= 0) {

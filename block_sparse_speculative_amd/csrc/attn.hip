@@ -1033,7 +1033,12 @@ hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
 template <bool BF16>
 hipError_t launch_dtype(const AttnParams& p, hipStream_t stream) {
   if constexpr (BF16) {
-    const bool t64 = attn_tile_tokens(p.bs, true) == 64;
+    const int tt = attn_tile_tokens(p.bs, true, p.R);
+    if (tt == 128) {   // 128-row units only: one workgroup per CU, 128 KB ring of 2 tiles
+      if (p.D == 128) return launch_cfg<Cfg<true, 128, 128, 128, 128>>(p, stream);
+      return launch_cfg<Cfg<true, 64, 128, 128, 128>>(p, stream);
+    }
+    const bool t64 = tt == 64;
     if (p.D == 128)
       return t64 ? launch_rows<true, 128, 64>(p, stream) : launch_rows<true, 128, 32>(p, stream);
     return t64 ? launch_rows<true, 64, 64>(p, stream) : launch_rows<true, 64, 32>(p, stream);

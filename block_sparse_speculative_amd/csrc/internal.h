@@ -92,9 +92,11 @@ enum : int32_t {
 // (cus = compute units of the device).
 int attn_merge_mode(int splits, int units, int rows, bool bf16, int cus);
 
-// Tokens per attention tile (a tile never spans two blocks): 64 for bf16 blocks of
-// 64 or more tokens, else 32.
-inline int attn_tile_tokens(int block_size, bool bf16) {
+// Tokens per attention tile (a tile never spans two blocks): for bf16, 128 when the
+// blocks hold 128 tokens and a unit has more than 64 rows (fewer tile barriers for the
+// compute-heavy 128-row units), else 64 for blocks of 64 or more tokens; 32 otherwise.
+inline int attn_tile_tokens(int block_size, bool bf16, int rows) {
+  if (bf16 && block_size >= 128 && rows > 64) return 128;
   return (bf16 && block_size >= 64) ? 64 : 32;
 }
 

@@ -154,7 +154,8 @@ sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const
 /* Number of KV splits sv_sparse_verify_attn uses: `num_splits` if > 0 (clamped to
  * the work available), else the library's choice for this shape. The k_max * (bs/TT)
  * tile slots of a (sequence, KV head) are cut into that many balanced ranges, where
- * TT = 64 tokens for bf16 blocks of 64 or more tokens, else 32. With more than one
+ * TT = 128 tokens for bf16 blocks of 128 tokens when T*G > 64, else 64 for bf16
+ * blocks of 64 or more tokens, else 32. With more than one
  * split, one extra workgroup per (sequence, KV head) handles the draft tokens. */
 int32_t sv_attn_num_splits(const sv_shape* shape, int32_t k_max, int32_t num_splits);
 

@@ -119,8 +119,13 @@ def test_split_count_and_workspace_size():
     rows, d, units = 8 * 4, 128, 8
     assert s4 == 4
     assert sv.attn_workspace_bytes(shape, 64, 4) >= units * 4 * rows * (d + 2) * 4
-    # bs 128 uses two 64-token tiles per block
+    # bs 128 uses two 64-token tiles per block at up to 64 rows per unit, one
+    # 128-token tile per block above that
     assert sv.attn_num_splits(_shape(num_seqs=1, block_size=128), 64, 10_000) == 128
+    assert sv.attn_num_splits(_shape(num_seqs=1, block_size=128, num_draft=16,
+                                     num_q_heads=64), 64, 10_000) == 64
+    assert sv.attn_num_splits(_shape(num_seqs=1, block_size=128, num_draft=16,
+                                     num_q_heads=64, dtype=sv.SV_F32), 64, 10_000) == 256
 
 
 def test_select_rejects_bad_budget_and_workspace():
