@@ -120,7 +120,7 @@ inline int attn_padded_rows(int rows) {
   return rows <= 16 ? 16 : rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
 }
 
-constexpr int kSelectChunk = 128;     // blocks scored by one select workgroup
+constexpr int kSelectChunk = 128;     // blocks scored by one select workgroup (at most)
 // Longest block-table row whose top-k one workgroup does with its keys in registers
 // (the fused select-and-attend mode needs it; longer rows take the separate LDS
 // top-k kernel).

@@ -5,10 +5,11 @@
 // Figure 1 caption).
 //
 // Two launches.
-//  score_kernel  grid = (ceil(NB / 128) chunks, Hkv, B): workgroup (c, g, b) scores
-//                blocks [128c, 128c+128) of sequence b for KV head g, streaming the
+//  score_kernel  grid = (ceil(NB / C) chunks, Hkv, B), C = 128 blocks (32 when that
+//                grid would leave most CUs idle): workgroup (c, g, b) scores
+//                blocks [Cc, Cc+C) of sequence b for KV head g, streaming the
 //                float32 representatives through the block table (one 16-byte load
-//                per lane, D/4 lanes per block, shuffle reduction in a fixed order).
+//                per lane, D/4 lanes per block, DPP reduction in a fixed order).
 //                Sequences whose budget keeps every block are skipped unless the
 //                caller asked for the scores.
 //  top-k         grid = (Hkv, B): budget, then
@@ -28,6 +29,14 @@ constexpr int NWAVE = NT / 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// x moved across lanes by the DPP control CTRL on the rows in ROW_MASK; lanes whose
+// source lies outside their row, and rows outside the mask, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
 }
 
 // Block-wide exclusive scan of one int per thread; returns the prefix and sets
@@ -59,14 +68,14 @@ __device__ __forceinline__ int budget_of(const SelectParams& p, int ctx, int nb)
   return budget_blocks_dev(ctx, nb, p.dense_ctx, p.min_blocks, p.frac_per_mille);
 }
 
-template <typename E, int D>
+template <typename E, int D, int CHUNK>
 __global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   // Linear workgroup id -> (unit, chunk); with xcd_group the workgroups of unit u
   // have linear ids congruent to u mod 8, the XCD its attention workgroups use.
-  const int nchunk = (p.NB + kSelectChunk - 1) / kSelectChunk;
+  const int nchunk = (p.NB + CHUNK - 1) / CHUNK;
   int unit, chunk;
   {
     const int lin = blockIdx.x;
@@ -91,10 +100,11 @@ __global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
   // ------------------------------------------------------------ scoring
   constexpr int LPB = D / 4;                   // lanes per block (one float4 each)
   constexpr int BPW = 64 / LPB;                // blocks per wave per pass
-  constexpr int PASSES = kSelectChunk / (NWAVE * BPW);
+  constexpr int PASSES = CHUNK / (NWAVE * BPW);
+  static_assert(PASSES >= 1 && CHUNK % (NWAVE * BPW) == 0, "chunk must fill the passes");
   const int sub = lane / LPB;
   const int li = lane % LPB;
-  const int j0 = chunk * kSelectChunk;
+  const int j0 = chunk * CHUNK;
   // A sequence whose budget keeps every block needs no scores.
   const bool dense = budget_of(p, ctx, nb) >= nb;
   if (j0 < nb && (!dense || p.scores_requested)) {
@@ -142,11 +152,17 @@ __global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
       d = __builtin_fmaf(qs[1], r[u].y, d);
       d = __builtin_fmaf(qs[2], r[u].z, d);
       d = __builtin_fmaf(qs[3], r[u].w, d);
-#pragma unroll
-      for (int off = LPB / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off, 64);
+      // Sum over the block's LPB lanes with DPP (no LDS round trip): prefix sums
+      // within each 16-lane row leave the row's total in its last lane; when a block
+      // spans two rows, the second row then adds the first row's total.
+      d += dpp_f32<0x111, 0xF>(d);   // row_shr:1
+      d += dpp_f32<0x112, 0xF>(d);   // row_shr:2
+      d += dpp_f32<0x114, 0xF>(d);   // row_shr:4
+      d += dpp_f32<0x118, 0xF>(d);   // row_shr:8
+      if constexpr (LPB == 32) d += dpp_f32<0x142, 0xA>(d);   // row_bcast:15 into rows 1, 3
       const bool ok = ph[u] >= 0 && ph[u] < p.P;
       d = ok ? d : 0.0f;
-      if (li == 0 && jj[u] < nb) sc[jj[u]] = d;
+      if (li == LPB - 1 && jj[u] < nb) sc[jj[u]] = d;
     }
   }
 
@@ -288,20 +304,31 @@ __global__ __launch_bounds__(NT) void topk_kernel(SelectParams p) {
 
 }  // namespace
 
-hipError_t launch_score(const SelectParams& p, bool bf16, hipStream_t stream) {
-  if (p.B == 0) return hipSuccess;
-  dim3 grid((p.NB + kSelectChunk - 1) / kSelectChunk * p.Hkv * p.B);
+template <int CHUNK>
+void launch_score_chunk(const SelectParams& p, bool bf16, hipStream_t stream) {
+  dim3 grid((p.NB + CHUNK - 1) / CHUNK * p.Hkv * p.B);
   if (bf16) {
     if (p.D == 128)
-      hipLaunchKernelGGL((score_kernel<uint16_t, 128>), grid, dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL((score_kernel<uint16_t, 128, CHUNK>), grid, dim3(NT), 0, stream, p);
     else
-      hipLaunchKernelGGL((score_kernel<uint16_t, 64>), grid, dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL((score_kernel<uint16_t, 64, CHUNK>), grid, dim3(NT), 0, stream, p);
   } else {
     if (p.D == 128)
-      hipLaunchKernelGGL((score_kernel<float, 128>), grid, dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL((score_kernel<float, 128, CHUNK>), grid, dim3(NT), 0, stream, p);
     else
-      hipLaunchKernelGGL((score_kernel<float, 64>), grid, dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL((score_kernel<float, 64, CHUNK>), grid, dim3(NT), 0, stream, p);
   }
+}
+
+hipError_t launch_score(const SelectParams& p, bool bf16, hipStream_t stream) {
+  if (p.B == 0) return hipSuccess;
+  // Blocks per workgroup: kSelectChunk, or a quarter of it when that would leave
+  // most of the CUs idle (few units, e.g. 8 of them over 1024 blocks).
+  const int64_t units = static_cast<int64_t>(p.B) * p.Hkv;
+  if (units * ((p.NB + kSelectChunk - 1) / kSelectChunk) < kAttnCUs)
+    launch_score_chunk<kSelectChunk / 4>(p, bf16, stream);
+  else
+    launch_score_chunk<kSelectChunk>(p, bf16, stream);
   return hipGetLastError();
 }
 
