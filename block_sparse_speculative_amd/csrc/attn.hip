@@ -88,10 +88,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// One 16-byte LDS-DMA load per lane: lane i's 16 bytes at `src` land at LDS byte
-// address lds + 16*i (lds is wave-uniform).
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+// One 16-byte LDS-DMA load per lane: lane i's 16 bytes at base + off land at LDS
+// byte address lds + 16*i. base and lds are wave-uniform (the base sits in an SGPR
+// pair), so a lane keeps one 32-bit offset per load rather than a 64-bit pointer.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(lds)
                : "memory", "m0");
 }
 
@@ -682,8 +684,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
   };
 
   // Per-lane source offsets of the LPW context-tile loads: the same for every tile
-  // (only the block base changes), so they are computed once.
-  int dma_off[C::LPW];
+  // (only the block base changes), so they are computed once, as 32-bit offsets from
+  // the wave-uniform block base.
+  uint32_t dma_off[C::LPW];
 #pragma unroll
   for (int u = 0; u < C::LPW; ++u) {
     const int cbase = (u * C::NWAVE + wave) * 64;
@@ -711,7 +714,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
         const int r = q / C::NCHK;
         const int cc = (q % C::NCHK) ^ swz_k<C::NCHK>(r);
         const char* base = cbase < C::KCH ? kdraft : vdraft;
-        dma16(base + (r < p.T ? r : 0) * draft_row + cc * 16, lbase + cbase * 16);
+        dma16s(base, static_cast<uint32_t>((r < p.T ? r : 0) * draft_row + cc * 16),
+               lbase + cbase * 16);
       }
     } else {
       int phys, tt0, nv;
@@ -722,7 +726,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int u = 0; u < C::LPW; ++u) {
         const int cbase = (u * C::NWAVE + wave) * 64;
-        dma16((cbase < C::KCH ? kb : vb) + dma_off[u], lbase + cbase * 16);
+        dma16s(cbase < C::KCH ? kb : vb, dma_off[u], lbase + cbase * 16);
       }
     }
   };
