@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--draft-tree", default="chain", choices=["chain", "random", "star"],
                     help="draft structure: a chain (the workload's own) or a seeded draft tree")
+    ap.add_argument("--launch-curve", action="store_true",
+                    help="also time the attention entry point against the number of selected "
+                         "blocks per unit (fixed cost and streaming rate of one launch)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -228,6 +231,88 @@ def dense_vs_sparse(inst, sparse_us: float, reps: int):
     }
 
 
+def launch_curve(inst, reps: int):
+    """Average time of one attention launch against k, the blocks selected per unit
+    (a seeded random sorted subset per sequence and KV head, distinct per layer), over
+    up to 8 layers of `inst` replayed in a graph. k runs from 0 to the workload's k_max
+    at its own split layout, then doubles with k_max = k up to every block. A least-
+    squares line through the points with k >= k_max gives the launch's fixed cost
+    (intercept) and its streaming rate (slope)."""
+    import torch
+    from block_sparse_speculative_amd import _lib as L
+    from block_sparse_speculative_amd import pipeline as PL
+
+    w = inst.w
+    B, Hkv = w.num_seqs, w.num_kv_heads
+    nbs = [-(-c // w.block_size) for c in inst.ctx_lens]
+    nl = min(8, len(inst.layers))
+    elem = 4 if w.dtype == "fp32" else 2
+    gen = torch.Generator().manual_seed(12345)
+    ks = sorted({0, max(1, inst.k_max // 8), max(1, inst.k_max // 4), max(1, inst.k_max // 2),
+                 inst.k_max})
+    k = inst.k_max * 2
+    while k < max(nbs):
+        ks.append(k)
+        k *= 2
+    ks.append(max(nbs))
+    points = []
+    for k in ks:
+        k_max = max(k, inst.k_max)
+        idxs = []
+        for _ in range(nl):
+            idx = torch.full((B, Hkv, k_max), -1, dtype=torch.int32)
+            for b, n in enumerate(nbs):
+                for g in range(Hkv):
+                    kk = min(k, n)
+                    idx[b, g, :kk] = torch.randperm(n, generator=gen)[:kk].sort().values.to(torch.int32)
+            idxs.append(idx.to(inst.device))
+        cnt = torch.tensor([min(k, n) for n in nbs], dtype=torch.int32)[:, None].expand(
+            B, Hkv).contiguous().to(inst.device)
+        ws = PL.Workspaces(inst.shape, k_max, 0, inst.device)
+        outs = [torch.empty_like(inst.layers[l].out) for l in range(nl)]
+
+        def call(l):
+            ly = inst.layers[l]
+            L.sparse_verify_attn(inst.shape, ly.q, ly.k_draft, ly.v_draft, ly.pool.k, ly.pool.v,
+                                 inst.table, inst.ctx, idxs[l], cnt, k_max, inst.scale, outs[l],
+                                 ws=ws.attn, draft_mask=inst.draft_mask)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for l in range(nl):
+                call(l)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for l in range(nl):
+                call(l)
+        stream = torch.cuda.current_stream()
+        graph.replay()
+        stream.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(stream)
+        ev1.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / (reps * nl)
+        kv = sum(min(k, n) * w.block_size for n in nbs) * Hkv * w.head_dim * 2 * elem
+        points.append({"k": k, "k_max": k_max, "splits": L.attn_num_splits(inst.shape, k_max, 0),
+                       "us": round(us, 2), "kv_bytes": kv, "gbs": round(kv / us / 1e3, 1)})
+        print(f"[bench]   launch curve k={k}: {us:.2f} us", file=sys.stderr, flush=True)
+    fit = [pt for pt in points if pt["k"] >= inst.k_max]
+    n = len(fit)
+    mx = sum(pt["kv_bytes"] for pt in fit) / n
+    my = sum(pt["us"] for pt in fit) / n
+    sxx = sum((pt["kv_bytes"] - mx) ** 2 for pt in fit)
+    slope = sum((pt["kv_bytes"] - mx) * (pt["us"] - my) for pt in fit) / sxx if sxx > 0 else 0.0
+    return {"points": points,
+            "fixed_us": my - slope * mx,
+            "stream_gbs": (1e-3 / slope) if slope > 0 else None}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -375,6 +460,9 @@ def main():
     if not args.no_dense:
         print("[bench] dense verification at the same context", file=sys.stderr, flush=True)
         result["dense_vs_sparse"] = dense_vs_sparse(inst0, attn_us, max(3, args.steps))
+    if args.launch_curve:
+        print("[bench] attention launch time against selected blocks", file=sys.stderr, flush=True)
+        result["launch_curve"] = launch_curve(inst0, max(3, args.steps))
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inst0, args.cpu_seconds)
