@@ -233,8 +233,10 @@ def dense_vs_sparse(inst, sparse_us: float, reps: int):
 
 def launch_curve(inst, reps: int):
     """Average time of one attention launch against k, the blocks selected per unit
-    (a seeded random sorted subset per sequence and KV head, distinct per layer), over
-    up to 8 layers of `inst` replayed in a graph. k runs from 0 to the workload's k_max
+    (a seeded random sorted subset per sequence and KV head, distinct per launch), over
+    8 launches replayed in a graph (cycling over the layers of `inst`, so a one-layer
+    workload does not carry a whole graph launch per attention launch). k runs from 0
+    to the workload's k_max
     at its own split layout, then doubles with k_max = k up to every block. A least-
     squares line through the points with k >= k_max gives the launch's fixed cost
     (intercept) and its streaming rate (slope)."""
@@ -245,7 +247,8 @@ def launch_curve(inst, reps: int):
     w = inst.w
     B, Hkv = w.num_seqs, w.num_kv_heads
     nbs = [-(-c // w.block_size) for c in inst.ctx_lens]
-    nl = min(8, len(inst.layers))
+    nl = len(inst.layers)
+    nlaunch = 8
     elem = 4 if w.dtype == "fp32" else 2
     gen = torch.Generator().manual_seed(12345)
     ks = sorted({0, max(1, inst.k_max // 8), max(1, inst.k_max // 4), max(1, inst.k_max // 2),
@@ -259,7 +262,7 @@ def launch_curve(inst, reps: int):
     for k in ks:
         k_max = max(k, inst.k_max)
         idxs = []
-        for _ in range(nl):
+        for _ in range(nlaunch):
             idx = torch.full((B, Hkv, k_max), -1, dtype=torch.int32)
             for b, n in enumerate(nbs):
                 for g in range(Hkv):
@@ -269,24 +272,24 @@ def launch_curve(inst, reps: int):
         cnt = torch.tensor([min(k, n) for n in nbs], dtype=torch.int32)[:, None].expand(
             B, Hkv).contiguous().to(inst.device)
         ws = PL.Workspaces(inst.shape, k_max, 0, inst.device)
-        outs = [torch.empty_like(inst.layers[l].out) for l in range(nl)]
+        outs = [torch.empty_like(inst.layers[i % nl].out) for i in range(nlaunch)]
 
-        def call(l):
-            ly = inst.layers[l]
+        def call(i):
+            ly = inst.layers[i % nl]
             L.sparse_verify_attn(inst.shape, ly.q, ly.k_draft, ly.v_draft, ly.pool.k, ly.pool.v,
-                                 inst.table, inst.ctx, idxs[l], cnt, k_max, inst.scale, outs[l],
+                                 inst.table, inst.ctx, idxs[i], cnt, k_max, inst.scale, outs[i],
                                  ws=ws.attn, draft_mask=inst.draft_mask)
 
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for l in range(nl):
-                call(l)
+            for i in range(nlaunch):
+                call(i)
         torch.cuda.current_stream().wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for l in range(nl):
-                call(l)
+            for i in range(nlaunch):
+                call(i)
         stream = torch.cuda.current_stream()
         graph.replay()
         stream.synchronize()
@@ -297,7 +300,7 @@ def launch_curve(inst, reps: int):
             graph.replay()
         ev1.record(stream)
         ev1.synchronize()
-        us = ev0.elapsed_time(ev1) * 1e3 / (reps * nl)
+        us = ev0.elapsed_time(ev1) * 1e3 / (reps * nlaunch)
         kv = sum(min(k, n) * w.block_size for n in nbs) * Hkv * w.head_dim * 2 * elem
         points.append({"k": k, "k_max": k_max, "splits": L.attn_num_splits(inst.shape, k_max, 0),
                        "us": round(us, 2), "kv_bytes": kv, "gbs": round(kv / us / 1e3, 1)})

@@ -6,7 +6,7 @@
 //
 // Two launches.
 //  score_kernel  grid = (ceil(NB / C) chunks, Hkv, B), C = 128 blocks (32 when that
-//                grid would leave most CUs idle): workgroup (c, g, b) scores
+//                grid would give a CU at most one workgroup): workgroup (c, g, b) scores
 //                blocks [Cc, Cc+C) of sequence b for KV head g, streaming the
 //                float32 representatives through the block table (one 16-byte load
 //                per lane, D/4 lanes per block, DPP reduction in a fixed order).
@@ -322,10 +322,12 @@ void launch_score_chunk(const SelectParams& p, bool bf16, hipStream_t stream) {
 
 hipError_t launch_score(const SelectParams& p, bool bf16, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
-  // Blocks per workgroup: kSelectChunk, or a quarter of it when that would leave
-  // most of the CUs idle (few units, e.g. 8 of them over 1024 blocks).
+  // Blocks per workgroup: kSelectChunk, or a quarter of it when kSelectChunk would
+  // give a CU at most one workgroup (8 units over 1024 blocks leave most CUs idle;
+  // 32 units give each CU one workgroup, whose two dependent round trips then move
+  // only 64 KB: four smaller workgroups per CU keep more loads in flight).
   const int64_t units = static_cast<int64_t>(p.B) * p.Hkv;
-  if (units * ((p.NB + kSelectChunk - 1) / kSelectChunk) < kAttnCUs)
+  if (units * ((p.NB + kSelectChunk - 1) / kSelectChunk) <= kAttnCUs)
     launch_score_chunk<kSelectChunk / 4>(p, bf16, stream);
   else
     launch_score_chunk<kSelectChunk>(p, bf16, stream);
