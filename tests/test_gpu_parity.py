@@ -85,6 +85,12 @@ SMALL = {
                                  budget=(0, 12, 0, 1, 1), plant_count=4),
     "fp32_rows32_bs128": W["tiny"].with_(num_draft=8, block_size=128, ctx=(4500,),
                                          budget=(0, 8, 0, 1, 1)),
+    # fp32 units of 64 and 128 rows (one workgroup per CU, 32-token tiles)
+    "fp32_rows64_d64": W["tiny"].with_(num_q_heads=16, num_kv_heads=2, num_draft=8,
+                                       ctx=(2500,)),
+    "fp32_rows128_d128": W["tiny"].with_(num_q_heads=16, num_kv_heads=2, num_draft=16,
+                                         head_dim=128, block_size=64, ctx=(3000,),
+                                         budget=(0, 12, 0, 1, 1)),
     # more than 1024 blocks per row: LDS radix top-k, and the fused call's fallback
     "long_table": W["llama32k"].with_(num_seqs=1, num_q_heads=8, num_kv_heads=2, block_size=32,
                                       ctx=(40000,)),
@@ -182,6 +188,7 @@ TREES = {
     "llama_small": SMALL["llama_small"],
     "qwen_small": SMALL["qwen_small"],                  # T = 16: all 16 mask bits in use
     "fp32_rows32_bs128": SMALL["fp32_rows32_bs128"],
+    "fp32_rows128_d128": SMALL["fp32_rows128_d128"],    # fp32, T = 16
     "edge": EDGE,                                       # ctx 0: the drafts alone
     "long_table": SMALL["long_table"],                  # > 1024 blocks: separate top-k
 }
