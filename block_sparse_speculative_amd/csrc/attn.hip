@@ -26,10 +26,13 @@
 // Data movement: tiles stream HBM -> LDS through 16-byte LDS-DMA loads
 // (global_load_lds_dwordx4) into a ring of NBUF buffers, so NBUF - 1 tiles are in
 // flight while one is computed (a 64 KB ring when two workgroups share a CU, else
-// 128 KB). The DMA is issued from inline assembly and waited for with explicit
-// vmcnt counts (every tile is exactly LPW loads per lane, and no other vector load
-// sits in the loop). LDS rows are XOR-swizzled in 16-byte chunks so the MFMA
-// operand reads (16 lanes, 16 rows, one chunk) hit distinct banks.
+// 128 KB). The DMA is issued from inline assembly (from a wave-uniform base in SGPRs
+// plus a 32-bit per-lane offset) and waited for with explicit vmcnt counts: every
+// tile is exactly LPW loads per lane. Any other vector memory access in the loop
+// (the register reloads of the fp32 128-row variants) only makes such a wait
+// stricter, never looser, since loads complete in issue order. LDS rows are
+// XOR-swizzled in 16-byte chunks so the MFMA operand reads (16 lanes, 16 rows, one
+// chunk) hit distinct banks.
 //
 // Compute, per wave (16 rows, a subset of a tile's 32-token groups):
 //   S^T = K Q^T      (MFMA, M = tokens, N = rows, K = head dim)
