@@ -305,15 +305,21 @@ def launch_curve(inst, reps: int):
         points.append({"k": k, "k_max": k_max, "splits": L.attn_num_splits(inst.shape, k_max, 0),
                        "us": round(us, 2), "kv_bytes": kv, "gbs": round(kv / us / 1e3, 1)})
         print(f"[bench]   launch curve k={k}: {us:.2f} us", file=sys.stderr, flush=True)
-    fit = [pt for pt in points if pt["k"] >= inst.k_max]
+    fixed_us, stream_gbs = fit_launch_line(points, inst.k_max)
+    return {"points": points, "fixed_us": fixed_us, "stream_gbs": stream_gbs}
+
+
+def fit_launch_line(points, k_min: int):
+    """Least-squares line us = fixed + kv_bytes / rate through the points with
+    k >= k_min. Returns (fixed cost in us, streaming rate in GB/s, or None when the
+    slope is not positive)."""
+    fit = [pt for pt in points if pt["k"] >= k_min]
     n = len(fit)
     mx = sum(pt["kv_bytes"] for pt in fit) / n
     my = sum(pt["us"] for pt in fit) / n
     sxx = sum((pt["kv_bytes"] - mx) ** 2 for pt in fit)
     slope = sum((pt["kv_bytes"] - mx) * (pt["us"] - my) for pt in fit) / sxx if sxx > 0 else 0.0
-    return {"points": points,
-            "fixed_us": my - slope * mx,
-            "stream_gbs": (1e-3 / slope) if slope > 0 else None}
+    return my - slope * mx, ((1e-3 / slope) if slope > 0 else None)
 
 
 def main():
