@@ -48,10 +48,11 @@
 //
 // Merge of the partials of a unit:  O = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
 //  - S == 1: the workgroup normalises and writes the output itself.
-//  - in-kernel (the whole grid resident at once): every workgroup writes its partial
-//    with device-scope stores, takes a device-scope arrival ticket, waits (bounded)
-//    for all workgroups of its unit, then merges its own slice of the unit's rows;
-//    the last of the departure increments clears the ticket.
+//  - in-kernel (the whole grid resident at once, at most 32 workgroups per unit):
+//    every workgroup writes its partial with device-scope stores, then a device-scope
+//    arrival tag (the unit's launch epoch + 1) in its slot of the unit's counter line;
+//    it waits (bounded) until every sibling's slot holds this launch's tag, merges its
+//    own slice of the unit's rows, and advances the epoch.
 //  - otherwise merge_kernel combines the partials in a second launch.
 //
 // XCD placement: workgroups are dispatched to the 8 XCDs round-robin by linear id.
@@ -527,6 +528,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
   // split's block indices or the unit's scores, and the query fragments.
   const cint_ptr s_ctx = (cint_ptr)(p.ctx_lens);
   int ctx = s_ctx[b];
+  // In-launch merge: the unit's launch epoch (this launch's arrival tags are epoch + 1).
+  uint32_t epoch = 0u;
+  if (p.merge == kMergeInKernel)
+    epoch = __hip_atomic_load(p.tickets + static_cast<int64_t>(unit) * kTicketStride + kEpochWord,
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int nsel_in = 0;
   if constexpr (!TOPK) {
     const cint_ptr s_cnt = (cint_ptr)(p.cnt);
@@ -918,22 +924,31 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
   }
   if (!ink) return;
 
-  // Arrival: this workgroup's partial has reached the device coherence point before
-  // its ticket is taken; then wait (bounded) until all NP workgroups of the unit have
-  // arrived. The launch only takes this mode when its whole grid is resident at
-  // once, so every sibling is running and the wait ends.
+  // Arrival: this workgroup's partial reaches the device coherence point, then its
+  // tag (the launch epoch + 1) goes to its slot of the unit's line, and wave 0 polls
+  // every sibling's slot (bounded) until all carry this launch's tag. Slots written by
+  // earlier launches hold older epochs, so nothing needs clearing. The launch only
+  // takes this mode when its whole grid is resident at once (every sibling is running,
+  // so the wait ends) and a unit has at most kMaxInKernelParts workgroups.
   wait_vmcnt<0>();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   lds_barrier();
+  uint32_t* line = p.tickets + static_cast<int64_t>(unit) * kTicketStride;
+  const uint32_t tag = __builtin_amdgcn_readfirstlane(epoch) + 1u;
   int* flag = reinterpret_cast<int*>(smem + C::FLAG_OFF);
-  if (tid == 0) {
-    uint32_t* ticket = p.tickets + static_cast<int64_t>(unit) * kTicketStride;
-    unsigned v = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    for (int spin = 0; v < static_cast<unsigned>(NP) && spin < kMergeSpinLimit; ++spin) {
+  if (tid == 0)
+    __hip_atomic_store(line + kTagWord0 + split, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave == 0) {
+    bool done = false;
+    for (int spin = 0; spin < kMergeSpinLimit; ++spin) {
+      const uint32_t t = lane < NP ? __hip_atomic_load(line + kTagWord0 + lane, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
+                                   : tag;
+      done = __builtin_amdgcn_ballot_w64(t != tag) == 0;
+      if (done) break;
       __builtin_amdgcn_s_sleep(8);
-      v = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    *flag = v >= static_cast<unsigned>(NP) ? 1 : 0;
+    if (lane == 0) *flag = done ? 1 : 0;
   }
   lds_barrier();
   const bool all_in = *flag != 0;
@@ -959,14 +974,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
     if (p.lse && dim == 0) p.lse[ob] = lse2 * kLn2;
   }
 
-  // Departure: the last of the unit's 2 * NP ticket increments resets the counter
-  // for the next launch.
-  if (tid == 0) {
-    uint32_t* ticket = p.tickets + static_cast<int64_t>(unit) * kTicketStride;
-    const unsigned d = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == static_cast<unsigned>(2 * NP - 1))
-      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // The next launch's epoch: every sibling read this one in its prologue before it
+  // wrote its tag, so any workgroup that has seen all tags may advance it (they all
+  // store the same value).
+  if (tid == 0 && all_in)
+    __hip_atomic_store(line + kEpochWord, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Combine the S partials of every (unit, row) in one pass over the splits, sixteen
@@ -1058,6 +1070,7 @@ hipError_t launch_dtype(const AttnParams& p, hipStream_t stream) {
 
 int attn_merge_mode(int splits, int units, int rows, bool bf16, int cus) {
   if (splits <= 1) return kMergeNone;
+  if (splits + 1 > kMaxInKernelParts) return kMergeKernel;   // one arrival tag per workgroup
   // workgroups the launch keeps resident per CU: two with the 64 KB ring (bf16), else one
   const int per_cu = (attn_ring_kb(splits, units, rows, bf16) == 64 && bf16) ? 2 : 1;
   const int64_t grid = static_cast<int64_t>(splits + 1) * units;

@@ -101,7 +101,12 @@ inline int attn_tile_tokens(int block_size, bool bf16, int rows) {
 }
 
 constexpr int kAttnCUs = 256;        // compute units of the MI355X
-constexpr int kTicketStride = 64;    // uint32 per merge counter: one 256-byte line each
+constexpr int kTicketStride = 64;    // uint32 per unit's merge line: one 256-byte line each
+// In-launch merge words of a unit's line: the launch epoch, and one arrival tag per
+// workgroup of the unit (so at most kMaxInKernelParts workgroups per unit).
+constexpr int kEpochWord = 1;
+constexpr int kTagWord0 = 32;
+constexpr int kMaxInKernelParts = kTicketStride - kTagWord0;
 constexpr int kXcds = 8;             // XCDs; workgroups are dispatched round-robin over them
 
 // Whether the per-unit kernels can place each unit on one XCD.

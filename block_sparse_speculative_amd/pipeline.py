@@ -64,7 +64,7 @@ class Workspaces:
         self.sel = torch.empty(max(L.select_workspace_bytes(shape, k_max), 1), dtype=torch.uint8,
                                device=device)
         n = L.attn_workspace_bytes(shape, k_max, num_splits)
-        # zero-filled once: the attention workspaces start with merge counters
+        # zero-filled once: the attention workspaces start with the merge words
         self.attn = torch.zeros(n, dtype=torch.uint8, device=device) if n else None
         self.fused = torch.zeros(L.select_and_attend_workspace_bytes(shape, k_max, num_splits),
                                  dtype=torch.uint8, device=device)

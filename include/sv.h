@@ -185,10 +185,12 @@ size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num
  * num_splits: 0 = library choice, else the number of KV splits (see
  * sv_attn_num_splits). With more than one split the partial results go to `ws`
  * (sv_attn_workspace_bytes() bytes; may be NULL when that is 0). Its first B*Hkv*256
- * bytes are merge counters that must be zero before the first call; every call that
- * completes leaves them zero (zero-fill the workspace once at allocation). When the
- * whole grid fits on the device at once, the workgroups of a (sequence, KV head)
- * wait for each other and merge inside the launch; otherwise a second kernel merges.
+ * bytes are merge words (per (sequence, KV head): a launch epoch and one arrival tag
+ * per workgroup). Zero-fill the workspace once at allocation and then leave those bytes
+ * to the library between calls (zero-filling all of them again is also valid; changing
+ * only some of them is not). When the whole grid fits on the device at once and a
+ * (sequence, KV head) has at most 32 workgroups, its workgroups wait for each other and
+ * merge inside the launch; otherwise a second kernel merges.
  * Calls that may run concurrently must not share a workspace. scale must be finite
  * and > 0. */
 sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,
@@ -218,8 +220,8 @@ size_t sv_select_and_attend_workspace_bytes(const sv_shape* shape, int32_t k_max
  *   arguments        as in sv_select_blocks and sv_sparse_verify_attn
  *   idx, cnt         outputs (as sv_select_blocks writes them)
  *   ws               sv_select_and_attend_workspace_bytes() bytes: the attention
- *                    workspace (merge counters first, zero before the first call and
- *                    left zero; zero-fill once at allocation), then the score scratch.
+ *                    workspace (merge words first: zero-fill once at allocation, then
+ *                    leave them to the library), then the score scratch.
  *                    Calls that may run concurrently must not share it. */
 sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
                                const float* repr_pool, const void* k_draft, const void* v_draft,
