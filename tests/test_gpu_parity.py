@@ -328,6 +328,40 @@ def test_run_to_run_bit_identical():
         assert torch.equal(x, y)
 
 
+def test_merge_tags_on_a_shared_workspace():
+    # The in-launch merge recognises a unit's workgroups by tags carrying the unit's
+    # launch epoch. Launches with different split counts on one workspace (tags of other
+    # split counts left in the slots), and a zero-fill of the whole workspace between
+    # calls, must give exactly what the same call gives on a fresh workspace.
+    _gpu()
+    from block_sparse_speculative_amd import _lib as L
+    inst = Instance(SMALL["llama_small"], seed=31)
+    inst.step()
+    torch.cuda.synchronize()
+    ly = inst.layers[0]
+    seq = [3, 7, 3, 11, 2, 7, 0, 3]
+    nbytes = max(L.attn_workspace_bytes(inst.shape, inst.k_max, s) for s in seq)
+    shared = torch.zeros(nbytes, dtype=torch.uint8, device=inst.device)
+
+    def call(splits, ws):
+        out, lse = torch.empty_like(ly.out), torch.empty_like(ly.lse)
+        L.sparse_verify_attn(inst.shape, ly.q, ly.k_draft, ly.v_draft, ly.pool.k, ly.pool.v,
+                             inst.table, inst.ctx, ly.idx, ly.cnt, inst.k_max, inst.scale, out,
+                             lse=lse, ws=ws, num_splits=splits)
+        return out, lse
+
+    for i, splits in enumerate(seq):
+        if i == 5:
+            shared.zero_()
+        a = call(splits, shared)
+        fresh = torch.zeros(max(L.attn_workspace_bytes(inst.shape, inst.k_max, splits), 1),
+                            dtype=torch.uint8, device=inst.device)
+        b = call(splits, fresh)
+        torch.cuda.synchronize()
+        assert torch.isfinite(a[0].float()).all(), f"splits {splits}"
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), f"splits {splits}"
+
+
 def test_paged_and_contiguous_tables_bit_identical():
     _gpu()
     w = SMALL["ragged_small"]
