@@ -39,6 +39,19 @@ class Budget(ctypes.Structure):
                 ("keep_last", ctypes.c_int32)]
 
 
+class AttnPlan(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("workgroups", ctypes.c_int32),
+                ("tile_tokens", ctypes.c_int32), ("padded_rows", ctypes.c_int32),
+                ("ring_kb", ctypes.c_int32), ("merge_mode", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+# sv_merge_mode
+MERGE_NONE, MERGE_IN_LAUNCH_WAIT, MERGE_IN_LAUNCH_LAST, MERGE_KERNEL = 0, 1, 2, 3
+
+
 class SvError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{_STATUS.get(status, status)}: {message}")
@@ -55,12 +68,13 @@ _SIG = [
     ("sv_status_str", ctypes.c_char_p, [_I]),
     ("sv_last_error", ctypes.c_char_p, []),
     ("sv_budget_blocks", _I, [ctypes.POINTER(Budget), _I, _I]),
-    ("sv_block_repr", _I, [ctypes.POINTER(Shape), _P, _P, _I, _P, _P, _P, _P, _P, _P, _P]),
+    ("sv_block_repr", _I, [ctypes.POINTER(Shape), _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     ("sv_select_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(Shape), _I]),
     ("sv_select_blocks", _I, [ctypes.POINTER(Shape), ctypes.POINTER(Budget), _P, _P, _P, _P, _I,
                               _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("sv_attn_num_splits", _I, [ctypes.POINTER(Shape), _I, _I]),
     ("sv_attn_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(Shape), _I, _I]),
+    ("sv_attn_plan_query", _I, [ctypes.POINTER(Shape), _I, _I, ctypes.POINTER(AttnPlan)]),
     ("sv_sparse_verify_attn", _I, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _I, ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     ("sv_select_and_attend_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(Shape), _I, _I]),
@@ -149,10 +163,21 @@ def attn_workspace_bytes(shape: Shape, k_max: int, num_splits: int = 0) -> int:
     return lib().sv_attn_workspace_bytes(ctypes.byref(shape), int(k_max), int(num_splits))
 
 
+def attn_plan(shape: Shape, k_max: int, num_splits: int = 0) -> dict:
+    """sv_attn_plan_query: splits, workgroups, tile tokens, padded rows, LDS ring and
+    merge mode of the attention launch for these arguments."""
+    plan = AttnPlan()
+    _check(lib().sv_attn_plan_query(ctypes.byref(shape), int(k_max), int(num_splits),
+                                    ctypes.byref(plan)))
+    return plan.as_dict()
+
+
 def block_repr(shape: Shape, k_new, v_new, n_new, ctx_before, block_table, k_pool, v_pool,
-               repr_pool):
-    """sv_block_repr: append k_new/v_new [B, n_new_max, Hkv, D] into the pool and
-    refresh the representatives of the touched blocks."""
+               repr_pool, ctx_after=None):
+    """sv_block_repr: write k_new/v_new [B, n_new_max, Hkv, D] into the pool at
+    ctx_before (an append, or a rewrite of cached tokens when ctx_after [B] gives the
+    sequence lengths afterwards) and refresh the representatives of the touched
+    blocks."""
     B, Hkv, D = shape.num_seqs, shape.num_kv_heads, shape.head_dim
     e = _elem(shape)
     n_new_max = int(k_new.shape[1])
@@ -163,11 +188,13 @@ def block_repr(shape: Shape, k_new, v_new, n_new, ctx_before, block_table, k_poo
     _dev(block_table, "block_table", torch.int32, (B, shape.max_blocks_per_seq))
     P, bs = shape.num_phys_blocks, shape.block_size
     _dev(k_pool, "k_pool", e, (P, Hkv, bs, D))
-    _dev(v_pool, "v_pool", e, (P, Hkv, D, bs))
+    _dev(v_pool, "v_pool", e, (P, Hkv, bs, D))
     _dev(repr_pool, "repr_pool", torch.float32, (P, Hkv, D))
+    if ctx_after is not None:
+        _dev(ctx_after, "ctx_after", torch.int32, (B,))
     _check(lib().sv_block_repr(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), n_new_max,
-                               _ptr(n_new), _ptr(ctx_before), _ptr(block_table), _ptr(k_pool),
-                               _ptr(v_pool), _ptr(repr_pool), _stream()))
+                               _ptr(n_new), _ptr(ctx_before), _ptr(ctx_after), _ptr(block_table),
+                               _ptr(k_pool), _ptr(v_pool), _ptr(repr_pool), _stream()))
 
 
 def select_blocks(shape: Shape, budget: Budget, q, repr_pool, block_table, ctx_lens, k_max: int,
@@ -205,7 +232,7 @@ def sparse_verify_attn(shape: Shape, q, k_draft, v_draft, k_pool, v_pool, block_
     _dev(k_draft, "k_draft", e, (B, T, Hkv, D))
     _dev(v_draft, "v_draft", e, (B, T, Hkv, D))
     _dev(k_pool, "k_pool", e, (P, Hkv, bs, D))
-    _dev(v_pool, "v_pool", e, (P, Hkv, D, bs))
+    _dev(v_pool, "v_pool", e, (P, Hkv, bs, D))
     _dev(block_table, "block_table", torch.int32, (B, shape.max_blocks_per_seq))
     _dev(ctx_lens, "ctx_lens", torch.int32, (B,))
     _dev(idx, "idx", torch.int32, (B, Hkv, k_max))
@@ -243,7 +270,7 @@ def select_and_attend(shape: Shape, budget: Budget, q, repr_pool, k_draft, v_dra
     _dev(k_draft, "k_draft", e, (B, T, Hkv, D))
     _dev(v_draft, "v_draft", e, (B, T, Hkv, D))
     _dev(k_pool, "k_pool", e, (P, Hkv, bs, D))
-    _dev(v_pool, "v_pool", e, (P, Hkv, D, bs))
+    _dev(v_pool, "v_pool", e, (P, Hkv, bs, D))
     _dev(block_table, "block_table", torch.int32, (B, shape.max_blocks_per_seq))
     _dev(ctx_lens, "ctx_lens", torch.int32, (B,))
     _dev(idx, "idx", torch.int32, (B, Hkv, k_max))

@@ -128,22 +128,41 @@ size_t select_ws_layout(const sv_shape* s, size_t* scores_off) {
   return align_up(units * s->max_blocks_per_seq * sizeof(float));
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static std::atomic<int> cached[64];
+// Compute units and wall-clock rate (kHz) of the current device, cached per device.
+struct DeviceInfo {
+  int cus;
+  int wall_khz;
+};
+
+DeviceInfo device_info() {
+  static std::atomic<int> cus_cache[64];
+  static std::atomic<int> khz_cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return sv::kAttnCUs;
-  int n = cached[dev].load(std::memory_order_relaxed);
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return DeviceInfo{sv::kAttnCUs, 100000};
+  int n = cus_cache[dev].load(std::memory_order_relaxed);
+  int khz = khz_cache[dev].load(std::memory_order_relaxed);
   if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = sv::kAttnCUs;
-    cached[dev].store(n, std::memory_order_relaxed);
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz <= 0)
+      khz = 100000;   // the 100 MHz constant clock of CDNA GPUs
+    khz_cache[dev].store(khz, std::memory_order_relaxed);
+    cus_cache[dev].store(n, std::memory_order_relaxed);
   }
-  return n;
+  return DeviceInfo{n, khz};
 }
 
-// Attention workspace: [merge counters: units x 256 B][partial O][partial (m, l)].
+// Bytes of the merge lines at the start of an attention workspace (one per unit).
+size_t merge_lines_bytes(const sv_shape* s) {
+  const size_t units = static_cast<size_t>(s->num_seqs) * s->num_kv_heads;
+  return align_up(units * sv::kTicketStride * sizeof(uint32_t));
+}
+
+// Attention workspace: [merge lines: units x 256 B][partial O][partial (m, l)]; nothing
+// with one split.
 size_t attn_ws_layout(const sv_shape* s, int splits, size_t* o_off, size_t* ml_off) {
   size_t o_dummy, ml_dummy;
   if (!o_off) o_off = &o_dummy;
@@ -155,7 +174,7 @@ size_t attn_ws_layout(const sv_shape* s, int splits, size_t* o_off, size_t* ml_o
   const size_t rows = static_cast<size_t>(s->num_draft) * (s->num_q_heads / s->num_kv_heads);
   const size_t units = static_cast<size_t>(s->num_seqs) * s->num_kv_heads;
   const size_t parts = static_cast<size_t>(splits) + 1;   // + the draft-only split
-  *o_off = align_up(units * sv::kTicketStride * sizeof(uint32_t));
+  *o_off = merge_lines_bytes(s);
   *ml_off = *o_off + align_up(units * parts * rows * s->head_dim * sizeof(float));
   return *ml_off + align_up(units * parts * rows * 2 * sizeof(float));
 }
@@ -227,14 +246,21 @@ sv::AttnParams attn_params(const sv_shape* shape, const void* q, const void* k_d
   p.R = shape->num_draft * p.G;
   p.xcd_group = sv::xcd_groupable(p.B * p.Hkv) ? 1 : 0;
   p.tickets = ws_need ? reinterpret_cast<uint32_t*>(w) : nullptr;
-  p.merge = sv::attn_merge_mode(splits, p.B * p.Hkv, p.R, shape->dtype == SV_BF16, device_cus());
+  const DeviceInfo dev = device_info();
+  p.merge = sv::attn_merge_mode(splits, p.B * p.Hkv, p.R, shape->dtype == SV_BF16, dev.cus);
+  p.merge_wait_ticks = static_cast<uint32_t>(static_cast<int64_t>(dev.wall_khz) *
+                                             sv::kMergeWaitUs / 1000);
   p.scale_log2 = scale * 1.44269504088896340736f;
   return p;
 }
 
-// Workspace of sv_select_and_attend: [attention partials][scores].
+// Workspace of sv_select_and_attend: [attention workspace][scores]. The merge lines are
+// reserved even with one split, so the scores never land on them whatever split
+// counts calls on one workspace use.
 size_t fused_ws_layout(const sv_shape* s, int splits, size_t* scores_off) {
-  *scores_off = align_up(attn_ws_layout(s, splits, nullptr, nullptr));
+  const size_t attn = attn_ws_layout(s, splits, nullptr, nullptr);
+  const size_t lines = merge_lines_bytes(s);
+  *scores_off = align_up(attn > lines ? attn : lines);
   size_t sc_off;
   return *scores_off + select_ws_layout(s, &sc_off);
 }
@@ -275,8 +301,8 @@ int32_t sv_budget_blocks(const sv_budget* budget, int32_t ctx_len, int32_t block
 
 sv_status sv_block_repr(const sv_shape* shape, const void* k_new, const void* v_new,
                         int32_t n_new_max, const int32_t* n_new, const int32_t* ctx_before,
-                        const int32_t* block_table, void* k_pool, void* v_pool, float* repr_pool,
-                        void* stream) {
+                        const int32_t* ctx_after, const int32_t* block_table, void* k_pool,
+                        void* v_pool, float* repr_pool, void* stream) {
   const char* what = "sv_block_repr";
   if (sv_status st = check_shape(shape, what)) return st;
   if (n_new_max < 0) return fail(SV_ERR_BAD_SHAPE, "%s: n_new_max < 0", what);
@@ -287,7 +313,8 @@ sv_status sv_block_repr(const sv_shape* shape, const void* k_new, const void* v_
   }
   if (n_new_max > static_cast<int64_t>(shape->max_blocks_per_seq) * shape->block_size)
     return fail(SV_ERR_BAD_SHAPE, "%s: n_new_max exceeds the sequence capacity", what);
-  sv::ReprParams p{k_new, v_new, n_new, ctx_before, block_table, k_pool, v_pool, repr_pool,
+  sv::ReprParams p{k_new, v_new, n_new, ctx_before, ctx_after, block_table, k_pool, v_pool,
+                   repr_pool,
                    shape->num_seqs, shape->num_kv_heads, shape->head_dim, shape->block_size,
                    shape->max_blocks_per_seq, shape->num_phys_blocks, n_new_max};
   return from_hip(sv::launch_block_repr(p, shape->dtype == SV_BF16,
@@ -338,6 +365,31 @@ size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num
   if (check_kmax(shape, k_max, "sv_attn_workspace_bytes") != SV_OK) return 0;
   size_t o_off, ml_off;
   return attn_ws_layout(shape, resolve_splits(shape, k_max, num_splits), &o_off, &ml_off);
+}
+
+sv_status sv_attn_plan_query(const sv_shape* shape, int32_t k_max, int32_t num_splits,
+                             sv_attn_plan* plan) {
+  const char* what = "sv_attn_plan_query";
+  if (sv_status st = check_shape(shape, what)) return st;
+  if (sv_status st = check_kmax(shape, k_max, what)) return st;
+  if (num_splits < 0) return fail(SV_ERR_BAD_SHAPE, "%s: num_splits < 0", what);
+  if (!plan) return fail(SV_ERR_NULL_ARG, "%s: plan is NULL", what);
+  const bool bf16 = shape->dtype == SV_BF16;
+  const int rows = shape->num_draft * (shape->num_q_heads / shape->num_kv_heads);
+  const int units = shape->num_seqs * shape->num_kv_heads;
+  const int splits = resolve_splits(shape, k_max, num_splits);
+  plan->num_splits = splits;
+  plan->workgroups = (splits > 1 ? splits + 1 : 1) * units;
+  plan->tile_tokens = sv::attn_tile_tokens(shape->block_size, bf16, rows);
+  plan->padded_rows = plan->tile_tokens == 128 ? 128 : sv::attn_padded_rows(rows);
+  plan->ring_kb = plan->tile_tokens == 128 ? 128 : sv::attn_ring_kb(splits, units, rows, bf16);
+  switch (sv::attn_merge_mode(splits, units, rows, bf16, device_info().cus)) {
+    case sv::kMergeNone: plan->merge_mode = SV_MERGE_NONE; break;
+    case sv::kMergeWait: plan->merge_mode = SV_MERGE_IN_LAUNCH_WAIT; break;
+    case sv::kMergeLast: plan->merge_mode = SV_MERGE_IN_LAUNCH_LAST; break;
+    default: plan->merge_mode = SV_MERGE_KERNEL; break;
+  }
+  return ok();
 }
 
 sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,

@@ -41,18 +41,21 @@
 //   reduction, and the accumulators are rescaled only when some row max moved
 //   O^T += V^T P^T   (MFMA, M = head dim, N = rows, K = tokens)
 // Token order inside a 32-token group is permuted so the S^T accumulator a lane
-// holds is exactly the P^T operand it feeds, and the pool's dim-major V blocks give
-// the matching V^T operand as one 16-byte LDS read. Full context tiles take a path
+// holds is exactly the P^T operand it feeds. V tiles stay token-major in LDS, as in
+// the pool, and the matching V^T operand comes from two transposing LDS reads
+// (ds_read_b64_tr_b16, 8 bf16 tokens of one head dim per lane). Full context tiles take a path
 // with no per-token masking. bf16 uses v_mfma_f32_16x16x32_bf16, fp32
 // v_mfma_f32_16x16x4_f32; accumulation is fp32.
 //
 // Merge of the partials of a unit:  O = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
 //  - S == 1: the workgroup normalises and writes the output itself.
-//  - in-kernel (the whole grid resident at once, at most 32 workgroups per unit):
-//    every workgroup writes its partial with device-scope stores, then a device-scope
-//    arrival tag (the unit's launch epoch + 1) in its slot of the unit's counter line;
-//    it waits (bounded) until every sibling's slot holds this launch's tag, merges its
-//    own slice of the unit's rows, and advances the epoch.
+//  - in the launch (at most 32 workgroups per unit): every workgroup stores its
+//    partial with device-scope stores and counts itself in the unit's arrival word.
+//    When the whole grid can be resident at once, each workgroup waits (bounded in
+//    time) until all siblings have arrived and merges its own slice of the unit's
+//    rows; a workgroup whose wait runs out hands its slice to the last arriver. When
+//    the grid cannot be resident, the last arriver merges every row at once. No
+//    workgroup ever waits for a sibling without a time bound.
 //  - otherwise merge_kernel combines the partials in a second launch.
 //
 // XCD placement: workgroups are dispatched to the 8 XCDs round-robin by linear id.
@@ -64,6 +67,10 @@
 #include "internal.h"
 #include "topk_wg.h"
 
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
+#error "attn.hip is written for gfx950: its transposing LDS reads, LDS-DMA and cache-policy bits"
+#endif
+
 namespace sv {
 namespace {
 
@@ -73,9 +80,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
 
 constexpr float kLn2 = 0.69314718055994530942f;
-// Polls of the sibling wait before a workgroup gives up (and writes NaN): about a
-// second, far beyond any real wait (the siblings are resident and streaming).
-constexpr int kMergeSpinLimit = 1 << 20;
 constexpr int kBtStageMax = 1024;    // block-table rows up to this length are staged in LDS
 static_assert(kWaveTopkMaxBlocks <= kBtStageMax, "the fused select mode reads the staged row");
 
@@ -95,9 +99,18 @@ __device__ __forceinline__ void lds_barrier() {
 // One 16-byte LDS-DMA load per lane: lane i's 16 bytes at base + off land at LDS
 // byte address lds + 16*i. base and lds are wave-uniform (the base sits in an SGPR
 // pair), so a lane keeps one 32-bit offset per load rather than a 64-bit pointer.
+// The base is passed through readfirstlane so that it is an SGPR pair even where the
+// register allocator has kept the (uniform) pointer in VGPRs. readfirstlane returns a
+// signed int: each half is converted to uint32_t before it is widened, so a low word
+// with bit 31 set is not sign-extended into the high word.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
-               "s"(lds)
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
+  const uint64_t sa = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+               "s"(reinterpret_cast<const void*>(sa)), "s"(lds)
                : "memory", "m0");
 }
 
@@ -216,11 +229,9 @@ struct Cfg {
   static constexpr int NT = 64 * NWAVE;
   static constexpr int NN = RW / 16;              // 16-row MFMA tiles per wave
   static constexpr int NMD = D / 16;              // 16-dim MFMA tiles of O^T
-  static constexpr int NCHK = D * ES / 16;        // 16-byte chunks per K row
-  static constexpr int NCHV = TT * ES / 16;       // 16-byte chunks per V^T row
-  static constexpr int KCH = TT * NCHK;
-  static constexpr int VCH = D * NCHV;
-  static constexpr int TILE_CH = KCH + VCH;
+  static constexpr int NCHK = D * ES / 16;        // 16-byte chunks per K or V row (a token)
+  static constexpr int KCH = TT * NCHK;           // chunks of the K half of a tile (V: as many)
+  static constexpr int TILE_CH = 2 * KCH;
   static constexpr int TILE_BYTES = TILE_CH * 16;
   static constexpr int LPW = TILE_CH / NT;        // LDS-DMA loads per lane per tile
   // Ring depth: RING_KB of tiles (64 when two workgroups share a CU, 128 when one
@@ -234,7 +245,6 @@ struct Cfg {
   static constexpr int NBUF = NBUF_VM < NBUF_LDS ? (NBUF_VM < NBUF_CAP ? NBUF_VM : NBUF_CAP)
                                                  : (NBUF_LDS < NBUF_CAP ? NBUF_LDS : NBUF_CAP);
   static constexpr int KFC = NCHK / 4;            // K chunks per lane (a quarter row)
-  static constexpr int VPM = BF16 ? 1 : 2;        // 16-byte V^T chunks per lane per md
   static constexpr int MERGE_BYTES = ((NTG - 1) * RP * D + 2 * NTG * RP) * 4;
   static constexpr int RING_BYTES =
       NBUF * TILE_BYTES > MERGE_BYTES ? NBUF * TILE_BYTES : MERGE_BYTES;
@@ -248,7 +258,7 @@ struct Cfg {
   static_assert(TILE_CH % NT == 0, "tile must split evenly over the lanes");
   static_assert(KCH % 64 == 0, "a wave load must not straddle K and V");
   static_assert((NBUF - 1) * LPW < 64, "vmcnt range");
-  static_assert(NCHK >= 8 && NCHV >= 4 && NCHV <= 16, "swizzle cases");
+  static_assert(NCHK >= 8 && NCHK <= 32, "swizzle cases");
 };
 
 template <int NCH>
@@ -259,14 +269,24 @@ __device__ __forceinline__ int swz_k(int r) {
   return NCH >= 16 ? mu : (mu >> 1);
 }
 
-// V^T rows (head dims) read together are 16 consecutive rows. For 128-byte rows the
-// XOR keeps both every 8-lane and every 16-lane phase of a 16-byte read on
-// distinct banks (row r and r+8 share parity, so they differ in the low bit).
-template <int NCH>
+// V rows (tokens) of a tile, XOR-swizzled in 16-byte chunks for the V^T operand reads.
+// bf16: a transposing read (ds_read_b64_tr_b16) makes each 16-lane group fetch 4 token
+// rows x 32 bytes (one pair of chunks), and the wave's four groups take rows 8*g4 + 4h
+// + 0..3 of a 32-token group. XOR-ing the pair index with a 3-bit function of the row
+// (2 bits for 128-byte rows, together with the row's parity) puts the 8 rows that
+// lanes 0-31 fetch, and those of lanes 32-63, on 8 distinct 32-byte bank windows, and
+// every 16-lane group's 4 rows on 4. fp32: one 4-byte read per lane; the 16 lanes of a
+// group read 64 bytes of row 8*g4 + jj, and XOR-ing the 64-byte window with g4 gives
+// the four groups distinct banks.
+template <class C>
 __device__ __forceinline__ int swz_v(int r) {
-  return NCH == 16 ? (r & 15)
-       : NCH == 8  ? ((r & 7) ^ ((r >> 3) & 1))
-                   : ((r & 15) >> 2);
+  if constexpr (C::BF16) {
+    const int f = C::NCHK >= 16 ? ((r & 3) | (((r >> 3) & 1) << 2))
+                                : (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+    return 2 * f;
+  } else {
+    return 4 * ((r >> 3) & 3);
+  }
 }
 
 // Token (within a 32-token group) held by MFMA M-row m of M-tile mt, chosen so that
@@ -301,18 +321,27 @@ struct WaveState {
   float l[C::NN];
 };
 
+// 4 x 16-bit elements per lane from LDS through the gfx950 transposing read: within
+// each 16-lane group, lane i receives element i % 4 of the 8 bytes fetched by lanes
+// i/4, i/4 + 4, i/4 + 8 and i/4 + 12 of the group (in that order).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(
+          (__attribute__((address_space(3))) char*)(const_cast<char*>(p))));
+}
+
 // One 32-token group of one tile for one wave. MASKED: tokens >= nvalid (and, for
 // the draft tile, drafts the row's draft does not see: bit u of tvis) are excluded.
-// DRAFT: V is token-major in LDS (the draft tile) instead of dim-major.
+// K and V are token-major in LDS ([TT][D], K rows swizzled by swz_k, V rows by swz_v).
 template <class C, bool MASKED, bool DRAFT>
 __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase,
                                              const char* vbase, int grp, int nvalid,
                                              const uint4 (&qf)[C::NN][C::KFC],
                                              const uint32_t (&tvis)[C::NN], float c, int l16,
                                              int g4) {
-  constexpr int ES = C::ES;
-  const int tok0 = grp * 32 + 8 * g4;
-  const int vc = (tok0 * ES) >> 4;
+  const int tok0 = grp * 32 + 8 * g4;   // the lane's 8 tokens: tok0 .. tok0 + 7
   // The group's K fragments are requested together; the V fragments are requested
   // once the S^T MFMAs are issued (they overlap the MFMAs and the softmax, and reuse
   // the K fragments' registers).
@@ -350,14 +379,39 @@ __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase
       sacc[mt][nt] = acc;
     }
   }
-  uint4 vf[C::NMD][C::VPM];
-  if constexpr (!DRAFT) {
+
+  // ---- V^T fragments: lane (g4, l16) needs head dim md*16 + l16 of tokens tok0..+7.
+  // bf16: two transposing reads per md (h = 0, 1); lane j of the 16-lane group g4
+  // fetches token row tok0 + 4h + j/4 at head dims md*16 + 4*(j%4) .. +3, so lane i of
+  // the group receives head dim md*16 + i of those 4 rows, in token order. fp32: one
+  // 4-byte read per (md, token).
+  constexpr int NV = C::BF16 ? 1 : 2;   // 16-byte registers per md
+  uint4 vf[C::NMD][NV];
 #pragma unroll
-    for (int md = 0; md < C::NMD; ++md) {
-      const int r = md * 16 + l16;
+  for (int md = 0; md < C::NMD; ++md) {
+    if constexpr (C::BF16) {
+      s16x4 half[2];
 #pragma unroll
-      for (int e = 0; e < C::VPM; ++e)
-        vf[md][e] = lds_read16(vbase, r * C::NCHV + ((vc + e) ^ swz_v<C::NCHV>(r)));
+      for (int h = 0; h < 2; ++h) {
+        const int r = tok0 + 4 * h + (l16 >> 2);
+        const int ch = 2 * md + ((l16 & 3) >> 1);
+        half[h] = lds_read_tr16(vbase + (r * C::NCHK + (ch ^ swz_v<C>(r))) * 16 + 8 * (l16 & 1));
+      }
+      vf[md][0] = __builtin_bit_cast(uint4, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3,
+                                                                   4, 5, 6, 7));
+    } else {
+      float v[8];
+      const int ch = md * 4 + (l16 >> 2);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int r = tok0 + jj;
+        v[jj] = *reinterpret_cast<const float*>(vbase + (r * C::NCHK + (ch ^ swz_v<C>(r))) * 16 +
+                                                4 * (l16 & 3));
+      }
+      vf[md][0] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                             __float_as_uint(v[3]));
+      vf[md][NV - 1] = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                  __float_as_uint(v[6]), __float_as_uint(v[7]));
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -401,74 +455,33 @@ __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase
   }
 
   // ---- O^T += V^T P^T
-  if constexpr (!DRAFT) {
-    if constexpr (C::BF16) {
-      bf16x8_t pf[C::NN];
+  if constexpr (C::BF16) {
+    bf16x8_t pf[C::NN];
+#pragma unroll
+    for (int nt = 0; nt < C::NN; ++nt)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) pf[nt][jj] = static_cast<__bf16>(pv[nt][jj]);
+#pragma unroll
+    for (int md = 0; md < C::NMD; ++md)
 #pragma unroll
       for (int nt = 0; nt < C::NN; ++nt)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pf[nt][jj] = static_cast<__bf16>(pv[nt][jj]);
-#pragma unroll
-      for (int md = 0; md < C::NMD; ++md)
-#pragma unroll
-        for (int nt = 0; nt < C::NN; ++nt)
-          st.o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, vf[md][0]), pf[nt], st.o[md][nt], 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int md = 0; md < C::NMD; ++md) {
-        const f32x4 v0 = __builtin_bit_cast(f32x4, vf[md][0]);
-        const f32x4 v1 = __builtin_bit_cast(f32x4, vf[md][C::VPM - 1]);
-#pragma unroll
-        for (int nt = 0; nt < C::NN; ++nt) {
-          f32x4 acc = st.o[md][nt];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[e], pv[nt][e], acc, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[e], pv[nt][4 + e], acc, 0, 0, 0);
-          st.o[md][nt] = acc;
-        }
-      }
-    }
+        st.o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, vf[md][0]), pf[nt], st.o[md][nt], 0, 0, 0);
   } else {
-    // Draft tile: V is token-major [TT][D] (K-style swizzle); gather the lane's 8
-    // tokens of one head dim element by element.
-    constexpr int EPC = 16 / ES;
 #pragma unroll
     for (int md = 0; md < C::NMD; ++md) {
-      const int dim = md * 16 + l16;
-      const int ch = dim / EPC;
-      const int off = (dim % EPC) * ES;
-      float v[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int r = tok0 + jj;
-        const char* src = vbase + (r * C::NCHK + (ch ^ swz_k<C::NCHK>(r))) * 16 + off;
-        if constexpr (C::BF16)
-          v[jj] = __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(src))
-                                  << 16);
-        else
-          v[jj] = *reinterpret_cast<const float*>(src);
-      }
+      const f32x4 v0 = __builtin_bit_cast(f32x4, vf[md][0]);
+      const f32x4 v1 = __builtin_bit_cast(f32x4, vf[md][NV - 1]);
 #pragma unroll
       for (int nt = 0; nt < C::NN; ++nt) {
-        if constexpr (C::BF16) {
-          bf16x8_t a, pf;
+        f32x4 acc = st.o[md][nt];
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            a[jj] = static_cast<__bf16>(v[jj]);
-            pf[jj] = static_cast<__bf16>(pv[nt][jj]);
-          }
-          st.o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, st.o[md][nt], 0, 0, 0);
-        } else {
-          f32x4 acc = st.o[md][nt];
+        for (int e = 0; e < 4; ++e)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[e], pv[nt][e], acc, 0, 0, 0);
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[jj], pv[nt][jj], acc, 0, 0, 0);
-          st.o[md][nt] = acc;
-        }
+        for (int e = 0; e < 4; ++e)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[e], pv[nt][4 + e], acc, 0, 0, 0);
+        st.o[md][nt] = acc;
       }
     }
   }
@@ -528,9 +541,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
   // split's block indices or the unit's scores, and the query fragments.
   const cint_ptr s_ctx = (cint_ptr)(p.ctx_lens);
   int ctx = s_ctx[b];
-  // In-launch merge: the unit's launch epoch (this launch's arrival tags are epoch + 1).
+  // In-launch merge: the unit's launch epoch (its parity picks the arrival word).
   uint32_t epoch = 0u;
-  if (p.merge == kMergeInKernel)
+  if (p.merge == kMergeWait || p.merge == kMergeLast)
     epoch = __hip_atomic_load(p.tickets + static_cast<int64_t>(unit) * kTicketStride + kEpochWord,
                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int nsel_in = 0;
@@ -700,29 +713,26 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
   for (int u = 0; u < C::LPW; ++u) {
     const int cbase = (u * C::NWAVE + wave) * 64;
     const int ch = cbase + lane;
-    if (cbase < C::KCH) {
-      const int r = ch / C::NCHK;
-      dma_off[u] = r * (D * ES) + ((ch % C::NCHK) ^ swz_k<C::NCHK>(r)) * 16;
-    } else {
-      const int q = ch - C::KCH;
-      const int r = q / C::NCHV;
-      dma_off[u] = r * p.bs * ES + ((q % C::NCHV) ^ swz_v<C::NCHV>(r)) * 16;
-    }
+    const bool is_k = cbase < C::KCH;
+    const int q = is_k ? ch : ch - C::KCH;
+    const int r = q / C::NCHK;
+    dma_off[u] = r * (D * ES) + ((q % C::NCHK) ^ (is_k ? swz_k<C::NCHK>(r) : swz_v<C>(r))) * 16;
   }
 
   auto issue = [&](int i, int buf) {
     const uint32_t lbase = smem_base + buf * C::TILE_BYTES;
     if (has_draft && i == 0) {
-      // Draft tile: K and V both token-major [TT][D]; rows >= T re-read draft 0
-      // (finite data, masked out of the softmax).
+      // Draft tile: rows are draft tokens, laid out as a context tile; rows >= T
+      // re-read draft 0 (finite data, masked out of the softmax).
 #pragma unroll
       for (int u = 0; u < C::LPW; ++u) {
         const int cbase = (u * C::NWAVE + wave) * 64;
         const int ch = cbase + lane;
-        const int q = cbase < C::KCH ? ch : ch - C::KCH;
+        const bool is_k = cbase < C::KCH;
+        const int q = is_k ? ch : ch - C::KCH;
         const int r = q / C::NCHK;
-        const int cc = (q % C::NCHK) ^ swz_k<C::NCHK>(r);
-        const char* base = cbase < C::KCH ? kdraft : vdraft;
+        const int cc = (q % C::NCHK) ^ (is_k ? swz_k<C::NCHK>(r) : swz_v<C>(r));
+        const char* base = is_k ? kdraft : vdraft;
         dma16s(base, static_cast<uint32_t>((r < p.T ? r : 0) * draft_row + cc * 16),
                lbase + cbase * 16);
       }
@@ -731,7 +741,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
       ctx_tile(i, phys, tt0, nv);
       const int64_t blk = static_cast<int64_t>(phys) * p.Hkv + g;
       const char* kb = kpool + (blk * p.bs + tt0) * D * ES;
-      const char* vb = vpool + blk * D * p.bs * ES + tt0 * ES;
+      const char* vb = vpool + (blk * p.bs + tt0) * D * ES;
 #pragma unroll
       for (int u = 0; u < C::LPW; ++u) {
         const int cbase = (u * C::NWAVE + wave) * 64;
@@ -740,21 +750,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
     }
   };
 
-  // Zero V^T columns of tokens >= nvalid in buffer buf (partly filled last block):
-  // the pool holds arbitrary bits there and P = 0 must not meet a NaN.
+  // Zero the V rows of tokens >= nvalid in buffer buf (partly filled last block): the
+  // pool holds arbitrary bits there and P = 0 must not meet a NaN.
   auto zero_tail = [&](int buf, int nvalid) {
     char* vbase = smem + buf * C::TILE_BYTES + C::KCH * 16;
-    const int ntail = TT - nvalid;
-    for (int e = tid; e < D * ntail; e += C::NT) {
-      const int r = e / ntail;
-      const int t = nvalid + (e - r * ntail);
-      const int cc = (t * ES) >> 4;
-      char* dst = vbase + (r * C::NCHV + (cc ^ swz_v<C::NCHV>(r))) * 16 + ((t * ES) & 15);
-      if constexpr (ES == 2)
-        *reinterpret_cast<uint16_t*>(dst) = 0;
-      else
-        *reinterpret_cast<uint32_t*>(dst) = 0u;
-    }
+    for (int e = nvalid * C::NCHK + tid; e < TT * C::NCHK; e += C::NT)
+      *reinterpret_cast<uint4*>(vbase + e * 16) = make_uint4(0u, 0u, 0u, 0u);
   };
 
   WaveState<C> st;
@@ -894,10 +895,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
 
   // Partial of this split: O (unnormalised), running max (log2 units), denominator.
   // kMergeKernel: plain stores for merge_kernel (with XCD grouping its workgroups for
-  // the unit run on the same XCD and find them in its L2). kMergeInKernel:
-  // device-scope stores, then every workgroup of the unit waits for its siblings
-  // and merges its own slice of rows.
-  const bool ink = p.merge == kMergeInKernel;
+  // the unit run on the same XCD and find them in its L2). kMergeWait / kMergeLast:
+  // device-scope stores, then the in-launch merge below.
+  const bool ink = p.merge == kMergeWait || p.merge == kMergeLast;
   const int part_bytes = NP * p.R * D * 4;
   const __amdgpu_buffer_rsrc_t po =
       make_rsrc(p.part_o + static_cast<int64_t>(unit) * NP * p.R * D, part_bytes);
@@ -924,61 +924,110 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
   }
   if (!ink) return;
 
-  // Arrival: this workgroup's partial reaches the device coherence point, then its
-  // tag (the launch epoch + 1) goes to its slot of the unit's line, and wave 0 polls
-  // every sibling's slot (bounded) until all carry this launch's tag. Slots written by
-  // earlier launches hold older epochs, so nothing needs clearing. The launch only
-  // takes this mode when its whole grid is resident at once (every sibling is running,
-  // so the wait ends) and a unit has at most kMaxInKernelParts workgroups.
+  // ---------------------------------------------------------------- in-launch merge
+  // Memory ordering. Partials cross workgroups (and XCDs) only through device-scope
+  // accesses: they are stored with sc1 buffer stores, which write through this XCD's
+  // L2, and the workgroup waits for those stores to complete (vmcnt(0)) before its
+  // arrival atomic; they are read back with sc1 buffer loads, which do not hit a
+  // stale line in the reader's L1 or L2. Together this stands in for a release
+  // (arrival) / acquire (seeing the arrival) pair at agent scope: since both sides
+  // carry the device scope themselves, no L2 writeback (buffer_wbl2) or invalidate
+  // (buffer_inv) is needed. The control words are agent-scope atomics.
+  //
+  // Protocol. Arrival word A = line[kArriveWord0 + 2 * (epoch & 1)]: low 32 bits count
+  // the unit's workgroups whose partials are stored, high 32 bits mark slices handed
+  // to the last arriver. Each workgroup adds 1 to A. The one that brings the count to
+  // NP is the last arriver: every partial is stored, and it merges its own slice plus
+  // every slice marked in the value it replaced. In kMergeWait every other workgroup
+  // polls A until the count reaches NP and then merges its own slice; if that takes
+  // longer than merge_wait_ticks (a sibling is not running: the grid is not resident,
+  // for instance because other kernels hold CUs), it marks its slice in A with a
+  // compare-and-swap and leaves, unless the count reached NP first. A mark can only
+  // precede the last arrival, so every slice is merged exactly once and no wait is
+  // unbounded. In kMergeLast the others leave at once and the last arriver merges all.
+  // The last arriver then clears the other arrival word (no workgroup of this launch
+  // uses it; every sibling read this launch's epoch before arriving) and advances the
+  // epoch, which the next launch on this workspace reads.
   wait_vmcnt<0>();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   lds_barrier();
   uint32_t* line = p.tickets + static_cast<int64_t>(unit) * kTicketStride;
-  const uint32_t tag = __builtin_amdgcn_readfirstlane(epoch) + 1u;
+  const uint32_t ep = __builtin_amdgcn_readfirstlane(epoch);
+  uint64_t* arrive = reinterpret_cast<uint64_t*>(line + kArriveWord0) + (ep & 1u);
   int* flag = reinterpret_cast<int*>(smem + C::FLAG_OFF);
-  if (tid == 0)
-    __hip_atomic_store(line + kTagWord0 + split, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (wave == 0) {
-    bool done = false;
-    for (int spin = 0; spin < kMergeSpinLimit; ++spin) {
-      const uint32_t t = lane < NP ? __hip_atomic_load(line + kTagWord0 + lane, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT)
-                                   : tag;
-      done = __builtin_amdgcn_ballot_w64(t != tag) == 0;
-      if (done) break;
-      __builtin_amdgcn_s_sleep(8);
+  // flag[0]: 0 = leave, 1 = merge the own slice, 2 = last arriver; flag[1]: handed slices.
+  if (tid == 0) {
+    const uint64_t old =
+        __hip_atomic_fetch_add(arrive, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int mode = 1;
+    uint32_t handed = 0u;
+    if (static_cast<uint32_t>(old) + 1u == static_cast<uint32_t>(NP)) {
+      mode = 2;
+      handed = static_cast<uint32_t>(old >> 32);
+    } else if (p.merge == kMergeLast) {
+      mode = 0;
+    } else {
+      const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + p.merge_wait_ticks;
+      for (;;) {
+        uint64_t cur = __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (static_cast<uint32_t>(cur) == static_cast<uint32_t>(NP)) break;
+        if (__builtin_amdgcn_s_memrealtime() > t_end) {
+          // Hand the slice over, unless the last sibling arrives first. A failed
+          // exchange means another workgroup changed A (an arrival or a hand-over, at
+          // most 2 * NP of them), so this loop ends.
+          while (static_cast<uint32_t>(cur) != static_cast<uint32_t>(NP)) {
+            const uint64_t want = cur | (1ull << (32 + split));
+            if (__hip_atomic_compare_exchange_strong(arrive, &cur, want, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+              mode = 0;
+              break;
+            }
+          }
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
     }
-    if (lane == 0) *flag = done ? 1 : 0;
+    flag[0] = mode;
+    flag[1] = static_cast<int>(handed);
   }
   lds_barrier();
-  const bool all_in = *flag != 0;
+  const int mode = __builtin_amdgcn_readfirstlane(flag[0]);
+  const uint32_t handed = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(flag[1]));
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (mode == 0) return;
 
-  // This workgroup's rows of the unit: [split * rpw, split * rpw + rpw).
-  const int rpw = (p.R + NP - 1) / NP;
-  const int rb = split * rpw;
-  const int re = rb + rpw < p.R ? rb + rpw : p.R;
-  for (int i4 = tid; i4 < (re - rb) * (D / 4); i4 += C::NT) {
-    const int row = rb + i4 / (D / 4);
-    const int dim = (i4 - (row - rb) * (D / 4)) * 4;
-    float lse2;
-    f32x4 v = combine_partials<kDeviceScope>(po, pml, NP, p.R, D, row, dim, &lse2);
-    if (!all_in) {   // a sibling never arrived: make the failure visible
-      v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      lse2 = __builtin_nanf("");
+  // Rows of slice s: [s * rpw, s * rpw + rpw) (kMergeLast: the last arriver takes all).
+  const int rpw = p.merge == kMergeLast ? p.R : (p.R + NP - 1) / NP;
+  auto merge_rows = [&](int rb, int re) {
+    for (int i4 = tid; i4 < (re - rb) * (D / 4); i4 += C::NT) {
+      const int row = rb + i4 / (D / 4);
+      const int dim = (i4 - (row - rb) * (D / 4)) * 4;
+      float lse2;
+      const f32x4 v = combine_partials<kDeviceScope>(po, pml, NP, p.R, D, row, dim, &lse2);
+      const int t = row / p.G;
+      const int h = g * p.G + (row - t * p.G);
+      const int64_t ob = (static_cast<int64_t>(b) * p.T + t) * p.Hq + h;
+      store_out4<C::BF16>(p.out, ob * D + dim, v);
+      if (p.lse && dim == 0) p.lse[ob] = lse2 * kLn2;
     }
-    const int t = row / p.G;
-    const int h = g * p.G + (row - t * p.G);
-    const int64_t ob = (static_cast<int64_t>(b) * p.T + t) * p.Hq + h;
-    store_out4<C::BF16>(p.out, ob * D + dim, v);
-    if (p.lse && dim == 0) p.lse[ob] = lse2 * kLn2;
+  };
+  auto slice = [&](int s_) {
+    const int rb = p.merge == kMergeLast ? 0 : s_ * rpw;
+    const int re = rb + rpw < p.R ? rb + rpw : p.R;
+    if (rb < re) merge_rows(rb, re);
+  };
+  slice(split);
+  if (mode == 2) {
+    if (p.merge == kMergeWait) {
+      for (uint32_t m = handed; m != 0u; m &= m - 1u) slice(__builtin_ctz(m));
+    }
+    if (tid == 0) {
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(line + kArriveWord0) + ((ep + 1u) & 1u), 0ull,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(line + kEpochWord, ep + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-
-  // The next launch's epoch: every sibling read this one in its prologue before it
-  // wrote its tag, so any workgroup that has seen all tags may advance it (they all
-  // store the same value).
-  if (tid == 0 && all_in)
-    __hip_atomic_store(line + kEpochWord, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Combine the S partials of every (unit, row) in one pass over the splits, sixteen
@@ -1070,11 +1119,11 @@ hipError_t launch_dtype(const AttnParams& p, hipStream_t stream) {
 
 int attn_merge_mode(int splits, int units, int rows, bool bf16, int cus) {
   if (splits <= 1) return kMergeNone;
-  if (splits + 1 > kMaxInKernelParts) return kMergeKernel;   // one arrival tag per workgroup
+  if (splits + 1 > kMaxInKernelParts) return kMergeKernel;   // one hand-over bit per workgroup
   // workgroups the launch keeps resident per CU: two with the 64 KB ring (bf16), else one
   const int per_cu = (attn_ring_kb(splits, units, rows, bf16) == 64 && bf16) ? 2 : 1;
   const int64_t grid = static_cast<int64_t>(splits + 1) * units;
-  return grid <= static_cast<int64_t>(cus) * per_cu ? kMergeInKernel : kMergeKernel;
+  return grid <= static_cast<int64_t>(cus) * per_cu ? kMergeWait : kMergeLast;
 }
 
 hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream) {

@@ -14,6 +14,7 @@ struct ReprParams {
   const void* v_new;
   const int32_t* n_new;
   const int32_t* ctx_before;
+  const int32_t* ctx_after;   // valid tokens after the call, or null (= ctx_before + n_new)
   const int32_t* block_table;
   void* k_pool;
   void* v_pool;
@@ -53,8 +54,9 @@ struct AttnParams {
   float* lse;
   float* part_o;        // [units, S+1, R, D] unnormalised partial outputs
   float* part_ml;       // [units, S+1, R, 2]  (running max in log2 units, denominator)
-  uint32_t* tickets;    // [units][kTicketStride] arrival/departure counters (one per line)
+  uint32_t* tickets;    // [units][kTicketStride] merge words (one 256-byte line per unit)
   int32_t merge;        // kMerge* mode
+  uint32_t merge_wait_ticks;   // kMergeWait: wall-clock ticks a workgroup waits for its siblings
   int32_t xcd_group;    // nonzero: the workgroups of unit u have linear ids = u mod 8
   int32_t B, Hq, Hkv, G, D, T, bs, NB, P, k_max;
   int32_t S;            // context splits (a draft-only split is added when S > 1)
@@ -85,11 +87,16 @@ hipError_t launch_reuse(const ReuseParams& p, hipStream_t stream);
 // How the split partials of a unit are combined.
 enum : int32_t {
   kMergeNone = 0,       // one split: the workgroup writes the output
-  kMergeInKernel = 1,   // the unit's workgroups wait for each other and merge slices
-  kMergeKernel = 2,     // a separate merge_kernel launch
+  kMergeWait = 1,       // in the launch: each workgroup waits (bounded) for its siblings and
+                        // merges its slice of rows; one that gives up hands its slice to the
+                        // last workgroup of the unit to arrive
+  kMergeLast = 2,       // in the launch: the last workgroup of a unit to arrive merges every
+                        // row; the others leave as soon as their partials are stored
+  kMergeKernel = 3,     // a separate merge_kernel launch
 };
-// Merge mode for a launch: in-kernel when the whole grid is resident at once
-// (cus = compute units of the device).
+// Merge mode for a launch (cus = compute units of the device): kMergeWait when the whole
+// grid can be resident at once, kMergeLast when it cannot, kMergeKernel when a unit has
+// more workgroups than the arrival word tracks.
 int attn_merge_mode(int splits, int units, int rows, bool bf16, int cus);
 
 // Tokens per attention tile (a tile never spans two blocks): for bf16, 128 when the
@@ -102,11 +109,15 @@ inline int attn_tile_tokens(int block_size, bool bf16, int rows) {
 
 constexpr int kAttnCUs = 256;        // compute units of the MI355X
 constexpr int kTicketStride = 64;    // uint32 per unit's merge line: one 256-byte line each
-// In-launch merge words of a unit's line: the launch epoch, and one arrival tag per
-// workgroup of the unit (so at most kMaxInKernelParts workgroups per unit).
-constexpr int kEpochWord = 1;
-constexpr int kTagWord0 = 32;
-constexpr int kMaxInKernelParts = kTicketStride - kTagWord0;
+// In-launch merge words of a unit's line: the launch epoch (uint32 word 0) and two 64-bit
+// arrival words (uint32 words 2-3 and 4-5), used by launches of even and odd epoch. An
+// arrival word holds the number of workgroups that have stored their partial (low 32
+// bits) and the slices handed to the last arriver (high 32 bits, bit s = split s), so a
+// unit has at most kMaxInKernelParts workgroups.
+constexpr int kEpochWord = 0;
+constexpr int kArriveWord0 = 2;
+constexpr int kMaxInKernelParts = 32;
+constexpr int kMergeWaitUs = 50;     // longest wait of a workgroup for its siblings
 constexpr int kXcds = 8;             // XCDs; workgroups are dispatched round-robin over them
 
 // Whether the per-unit kernels can place each unit on one XCD.

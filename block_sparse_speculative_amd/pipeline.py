@@ -18,7 +18,7 @@ from . import _lib as L
 class Pool:
     """Paged KV pool of one layer (layouts as documented in include/sv.h)."""
     k: torch.Tensor       # [P, Hkv, bs, D]
-    v: torch.Tensor       # [P, Hkv, D, bs]
+    v: torch.Tensor       # [P, Hkv, bs, D]
     reps: torch.Tensor    # [P, Hkv, D] float32
 
 
@@ -27,14 +27,17 @@ def alloc_pool(shape: L.Shape, device="cuda", fill_nan: bool = False) -> Pool:
     dt = torch.float32 if shape.dtype == L.SV_F32 else torch.bfloat16
     mk = torch.full if fill_nan else (lambda s, v, **kw: torch.empty(s, **kw))
     k = mk((P, Hkv, bs, D), float("nan"), dtype=dt, device=device)
-    v = mk((P, Hkv, D, bs), float("nan"), dtype=dt, device=device)
+    v = mk((P, Hkv, bs, D), float("nan"), dtype=dt, device=device)
     reps = mk((P, Hkv, D), float("nan"), dtype=torch.float32, device=device)
     return Pool(k, v, reps)
 
 
-def append(shape: L.Shape, pool: Pool, k_new, v_new, n_new, ctx_before, block_table):
-    """sv_block_repr over a batch of new tokens (k_new/v_new [B, n_max, Hkv, D])."""
-    L.block_repr(shape, k_new, v_new, n_new, ctx_before, block_table, pool.k, pool.v, pool.reps)
+def append(shape: L.Shape, pool: Pool, k_new, v_new, n_new, ctx_before, block_table,
+           ctx_after=None):
+    """sv_block_repr over a batch of new tokens (k_new/v_new [B, n_max, Hkv, D]); with
+    ctx_after the tokens rewrite cached positions of sequences of that length."""
+    L.block_repr(shape, k_new, v_new, n_new, ctx_before, block_table, pool.k, pool.v, pool.reps,
+                 ctx_after=ctx_after)
 
 
 def fill_pool(shape: L.Shape, pool: Pool, k_ctx, v_ctx, ctx_lens, block_table, chunk: int = 0):

@@ -40,11 +40,14 @@ class Instance:
                  ctx_lens: Optional[List[int]] = None, paged: Optional[bool] = None,
                  num_splits: int = 0, with_lse: bool = True, nan_pool: bool = False,
                  k_max: Optional[int] = None, append_chunk: int = 0, progress=None,
-                 fused: bool = False):
+                 fused: bool = False, layer_offset: int = 0):
         if paged is not None:
             w = w.with_(paged=paged)
         self.w = w
         self.seed = seed
+        # layer l of the instance is layer layer_offset + l of the workload (its inputs,
+        # and whether it selects or reuses)
+        self.layer_offset = layer_offset
         self.device = torch.device(device)
         self.ctx_lens = list(ctx_lens) if ctx_lens is not None else synth.context_lengths(w, seed)
         table, P = synth.block_table(w, self.ctx_lens, seed)
@@ -59,6 +62,7 @@ class Instance:
         self.scale = synth.softmax_scale(w)
         self.ws = PL.Workspaces(self.shape, self.k_max, num_splits, self.device)
         self.num_splits = L.attn_num_splits(self.shape, self.k_max, num_splits)
+        self.plan = L.attn_plan(self.shape, self.k_max, num_splits)
         self.fused = fused
         # Draft tree (None: chain drafts) and its visibility bits on the device.
         self.parents = synth.draft_parents(w, seed)
@@ -68,11 +72,11 @@ class Instance:
         B, T, Hq, Hkv, D = w.num_seqs, w.num_draft, w.num_q_heads, w.num_kv_heads, w.head_dim
         self.layers: List[Layer] = []
         for l in range(n_layers):
-            x = synth.make_layer(w, seed, l, self.device, self.ctx_lens)
+            x = synth.make_layer(w, seed, layer_offset + l, self.device, self.ctx_lens)
             pool = PL.alloc_pool(self.shape, self.device, fill_nan=nan_pool)
             PL.fill_pool(self.shape, pool, x["k_ctx"], x["v_ctx"], self.ctx_lens, self.table,
                          chunk=append_chunk)
-            reuse = w.reuse_odd_layers and l % 2 == 1
+            reuse = w.reuse_odd_layers and (layer_offset + l) % 2 == 1 and l > 0
             if reuse and fused:
                 idx, cnt = self.layers[l - 1].idx, self.layers[l - 1].cnt
             else:
@@ -89,8 +93,10 @@ class Instance:
                 progress(l + 1, n_layers)
 
     def logical(self, layer: int):
-        """Regenerate layer `layer`'s logical (unpaged) inputs on the device."""
-        return synth.make_layer(self.w, self.seed, layer, self.device, self.ctx_lens)
+        """Regenerate the logical (unpaged) inputs of the instance's layer `layer` on the
+        device."""
+        return synth.make_layer(self.w, self.seed, self.layer_offset + layer, self.device,
+                                self.ctx_lens)
 
     def select_or_reuse(self, l: int, scores: Optional[torch.Tensor] = None):
         ly = self.layers[l]

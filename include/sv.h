@@ -32,7 +32,7 @@
  *      NB  = max_blocks_per_seq   P  = num_phys_blocks
  *  - Paged KV pool (one pool per layer):
  *      k_pool    [P, Hkv, bs, D]  element type `dtype` (token-major in a block)
- *      v_pool    [P, Hkv, D, bs]  element type `dtype` (dim-major in a block)
+ *      v_pool    [P, Hkv, bs, D]  element type `dtype` (token-major in a block)
  *      repr_pool [P, Hkv, D]      float32, mean key of each block
  *    block_table [B, NB] int32 maps logical block j of sequence b to a physical
  *    block; only entries j < ceil(ctx_b / bs) are read.
@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 2
+#define SV_ABI_VERSION 3
 
 typedef enum sv_status {
   SV_OK = 0,
@@ -107,23 +107,31 @@ int32_t sv_budget_blocks(const sv_budget* budget, int32_t ctx_len, int32_t block
 
 /* KV append fused with the block-representative update (representative value of a
  * block: sciencestack page, Figure 1 caption; the pages leave it undefined and this
- * library takes the arithmetic mean of the block's keys over its valid tokens).
+ * library takes the arithmetic mean of the block's keys over its valid tokens). The
+ * same call rewrites tokens already in the cache, as the refresh after a periodic
+ * full verification does (SpecPV page, highlights and introduction: periodic full
+ * verification keeps errors from accumulating).
  *
  * For each sequence b, the n_new[b] tokens k_new[b, 0:n_new[b]] / v_new[...] are
  * written at logical positions ctx_before[b] .. ctx_before[b]+n_new[b]-1 of the
- * pool through block_table. Then, for every block touched, repr_pool receives the
- * float32 mean of ALL its valid keys (old and new), summed in slot order, so a
- * block's representative does not depend on how its tokens arrived.
+ * pool through block_table. The sequence then holds end_b valid tokens: ctx_after[b]
+ * when ctx_after is given (tokens past the rewritten ones stay valid), else
+ * ctx_before[b]+n_new[b] (an append). For every block touched, repr_pool receives the
+ * float32 mean of ALL its valid keys (old and new). The summation order depends only
+ * on the block's valid-token count, so a block's representative does not depend on
+ * how its tokens arrived.
  *   k_new, v_new  [B, n_new_max, Hkv, D]  dtype
  *   n_new         [B] int32, 0 <= n_new[b] <= n_new_max      (device)
  *   ctx_before    [B] int32, ctx_before[b]+n_new[b] <= NB*bs (device)
+ *   ctx_after     [B] int32 or NULL, ctx_before[b]+n_new[b] <= ctx_after[b] <= NB*bs
+ *                 (device; values outside that range are clamped into it)
  *   block_table   [B, NB] int32                              (device)
  *   k_pool, v_pool, repr_pool  pool tensors (layouts above), updated in place.
  * n_new_max may be 0 (nothing is launched). */
 sv_status sv_block_repr(const sv_shape* shape, const void* k_new, const void* v_new,
                         int32_t n_new_max, const int32_t* n_new, const int32_t* ctx_before,
-                        const int32_t* block_table, void* k_pool, void* v_pool,
-                        float* repr_pool, void* stream);
+                        const int32_t* ctx_after, const int32_t* block_table, void* k_pool,
+                        void* v_pool, float* repr_pool, void* stream);
 
 /* Bytes of workspace sv_select_blocks needs for this shape. */
 size_t sv_select_workspace_bytes(const sv_shape* shape, int32_t k_max);
@@ -162,6 +170,36 @@ int32_t sv_attn_num_splits(const sv_shape* shape, int32_t k_max, int32_t num_spl
 /* Bytes of workspace sv_sparse_verify_attn needs (0 when one split is used). */
 size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num_splits);
 
+/* How the partials of a split (sequence, KV head) unit are combined. */
+typedef enum sv_merge_mode {
+  SV_MERGE_NONE = 0,            /* one split: no partials                                */
+  SV_MERGE_IN_LAUNCH_WAIT = 1,  /* in the attention launch: the unit's workgroups wait,
+                                   bounded in time, for each other and merge a slice of
+                                   rows each (a workgroup whose wait runs out hands its
+                                   slice to the last one to arrive)                       */
+  SV_MERGE_IN_LAUNCH_LAST = 2,  /* in the attention launch: the last workgroup of the unit
+                                   to arrive merges every row (grids that cannot be
+                                   resident at once)                                      */
+  SV_MERGE_KERNEL = 3           /* a second kernel (more than 32 workgroups per unit)     */
+} sv_merge_mode;
+
+/* Launch plan of the attention for a shape (host-only; reads the current device's
+ * compute-unit count, 256 if there is no device). */
+typedef struct sv_attn_plan {
+  int32_t num_splits;    /* context splits (sv_attn_num_splits)                        */
+  int32_t workgroups;    /* workgroups of the attention launch                         */
+  int32_t tile_tokens;   /* tokens per KV tile                                         */
+  int32_t padded_rows;   /* rows (draft token x GQA head) of a unit, padded            */
+  int32_t ring_kb;       /* LDS ring of one workgroup in KB                            */
+  int32_t merge_mode;    /* sv_merge_mode                                              */
+} sv_attn_plan;
+
+/* Fills *plan for sv_sparse_verify_attn / sv_select_and_attend with these arguments.
+ * Returns the same status as those calls would for a bad shape, k_max or num_splits;
+ * SV_ERR_NULL_ARG when plan is NULL. */
+sv_status sv_attn_plan_query(const sv_shape* shape, int32_t k_max, int32_t num_splits,
+                             sv_attn_plan* plan);
+
 /* Multi-draft attention over the shared selected blocks (sciencestack page,
  * Figure 1 caption: all draft tokens use the same selected block set; abstract:
  * draft tokens are verified in one parallel pass).
@@ -185,12 +223,13 @@ size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num
  * num_splits: 0 = library choice, else the number of KV splits (see
  * sv_attn_num_splits). With more than one split the partial results go to `ws`
  * (sv_attn_workspace_bytes() bytes; may be NULL when that is 0). Its first B*Hkv*256
- * bytes are merge words (per (sequence, KV head): a launch epoch and one arrival tag
- * per workgroup). Zero-fill the workspace once at allocation and then leave those bytes
- * to the library between calls (zero-filling all of them again is also valid; changing
- * only some of them is not). When the whole grid fits on the device at once and a
- * (sequence, KV head) has at most 32 workgroups, its workgroups wait for each other and
- * merge inside the launch; otherwise a second kernel merges.
+ * bytes (rounded up to 256) are merge lines, one per (sequence, KV head): a launch
+ * epoch and two arrival words. Zero-fill the workspace at allocation, and again
+ * before a call with more (sequence, KV head) units than any earlier call on it; in
+ * between leave those bytes to the library (zero-filling all of them again is also
+ * valid; changing only some of them is not). How the partials are merged is given by
+ * sv_attn_plan_query (sv_merge_mode); no workgroup waits for another without a time
+ * bound, so the result does not depend on other work running on the device.
  * Calls that may run concurrently must not share a workspace. scale must be finite
  * and > 0. */
 sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void* k_draft,
@@ -215,14 +254,14 @@ size_t sv_select_and_attend_workspace_bytes(const sv_shape* shape, int32_t k_max
  * each run the budget + top-k of their unit from the scores (exact, lowest index
  * wins ties) before streaming their share of the selected blocks; split 0 of each
  * unit writes idx / cnt. With NB > 1024 the separate top-k kernel runs between the
- * two instead. The split partials are merged inside the attention launch when its
- * grid is resident at once, else by a merge kernel after it.
+ * two instead. The split partials are merged as sv_attn_plan_query reports.
  *   arguments        as in sv_select_blocks and sv_sparse_verify_attn
  *   idx, cnt         outputs (as sv_select_blocks writes them)
  *   ws               sv_select_and_attend_workspace_bytes() bytes: the attention
- *                    workspace (merge words first: zero-fill once at allocation, then
- *                    leave them to the library), then the score scratch.
- *                    Calls that may run concurrently must not share it. */
+ *                    workspace (merge lines first, reserved even with one split:
+ *                    zero-fill at allocation and before a call with more units than
+ *                    any earlier one, else leave them to the library), then the score
+ *                    scratch. Calls that may run concurrently must not share it. */
 sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
                                const float* repr_pool, const void* k_draft, const void* v_draft,
                                const int32_t* draft_mask, const void* k_pool, const void* v_pool,

@@ -18,6 +18,25 @@ TOL = {"fp32": dict(max_abs=1e-4, mean_abs=1e-4), "bf16": dict(max_abs=1e-2, mea
 LSE_TOL = 1e-4
 NEAR_TIE_REL = 1e-5
 
+# Element-wise bound for bf16 outputs, derived from the two bf16 roundings the path
+# makes (unit roundoff u = 2^-8 for bf16's 8-bit significand; everything else is fp32):
+#  - each softmax weight p_i meets V as bf16(p_i) = p_i (1 + d_i), |d_i| <= u, while the
+#    denominator sums the fp32 p_i, so the output moves by at most u * sum p_i |v_i| /
+#    sum p_i = u * O_abs, where O_abs is attention with |V| in place of V;
+#  - the output is rounded to bf16: at most u * |O|.
+# Hence |O_gpu - O_ref| <= u (|O_ref| + O_abs), plus second-order and fp32 terms, covered
+# by a factor (1 + 2^-6) and 1e-6 absolute.
+BF16_U = 2.0 ** -8
+BF16_BOUND_FACTOR = 1.0 + 2.0 ** -6
+BF16_BOUND_ABS = 1e-6
+
+# Observed errors of every checked case, printed at the end of the test run.
+STATS = []
+
+
+def record(case: str, **fields):
+    STATS.append(dict(case=case, **fields))
+
 
 def log(msg):
     print(msg, flush=True)
@@ -89,7 +108,9 @@ def check_selection(gpu_sel, oracle_sel, scores, k, nb, keep_first, keep_last):
 def check_output(gpu_out, gpu_lse, u: UnitInputs, sel, bs: int, scale: float, dtype: str,
                  parents=None):
     """Compare one unit's GPU output [T, G, D] (and lse [T, G]) with the oracle run on
-    the same selection (and draft tree). Returns (max_abs, mean_abs)."""
+    the same selection (and draft tree). Returns a dict of the observed errors:
+    max_abs, mean_abs, rel (max_abs / RMS of the reference output), lse, and for bf16
+    bound (the largest error as a fraction of its element-wise bound)."""
     ref, ref_lse = O.verify_attention(u.q, u.k_ctx, u.v_ctx, u.k_draft, u.v_draft, [sel], bs,
                                       scale, parents=parents)
     err = np.abs(gpu_out - ref)
@@ -97,10 +118,25 @@ def check_output(gpu_out, gpu_lse, u: UnitInputs, sel, bs: int, scale: float, dt
     assert np.isfinite(gpu_out).all(), "non-finite output"
     assert err.max() <= tol["max_abs"], f"max-abs {err.max():.3e} > {tol['max_abs']}"
     assert err.mean() <= tol["mean_abs"], f"mean-abs {err.mean():.3e} > {tol['mean_abs']}"
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    out = dict(max_abs=float(err.max()) if err.size else 0.0,
+               mean_abs=float(err.mean()) if err.size else 0.0,
+               rel=float(err.max() / rms) if rms > 0 else 0.0)
+    if dtype == "bf16" and err.size:
+        ref_abs, _ = O.verify_attention(u.q, u.k_ctx, np.abs(u.v_ctx), u.k_draft,
+                                        np.abs(u.v_draft), [sel], bs, scale, parents=parents)
+        bound = BF16_U * BF16_BOUND_FACTOR * (np.abs(ref) + ref_abs) + BF16_BOUND_ABS
+        frac = err / bound
+        worst = np.unravel_index(int(np.argmax(frac)), frac.shape)
+        assert frac.max() <= 1.0, (
+            f"bf16 element bound exceeded at {worst}: error {err[worst]:.3e}, bound "
+            f"{bound[worst]:.3e} (|O| {abs(ref[worst]):.3e}, O_abs {ref_abs[worst]:.3e})")
+        out["bound"] = float(frac.max())
     if gpu_lse is not None:
-        lerr = np.abs(gpu_lse - ref_lse).max()
+        lerr = np.abs(gpu_lse - ref_lse).max() if ref_lse.size else 0.0
         assert lerr <= LSE_TOL, f"lse error {lerr:.3e}"
-    return float(err.max()), float(err.mean())
+        out["lse"] = float(lerr)
+    return out
 
 
 def check_reps(gpu_reps, u: UnitInputs, bs: int, oracle_reps):
@@ -137,7 +173,10 @@ def verify_instance_units(inst, layer: int, units, logical=None, prev_sel=None, 
     lse = None if ly.lse is None else np64(ly.lse)
     G, bs = w.group, w.block_size
     kf, kl = w.budget[3], w.budget[4]
-    sels, stats = {}, {"exact": 0, "near-tie": 0, "max_abs": 0.0}
+    sels = {}
+    stats = {"units": 0, "exact": 0, "near-tie": 0, "max_abs": 0.0, "mean_abs": 0.0, "rel": 0.0,
+             "bound": 0.0, "lse": 0.0}
+    mean_sum = 0.0
     for (b, g) in units:
         u = unit_inputs(logical, b, g, G)
         nb = O.num_blocks(u.ctx, bs)
@@ -163,7 +202,11 @@ def verify_instance_units(inst, layer: int, units, logical=None, prev_sel=None, 
         gout = out[b, :, g * G:(g + 1) * G]
         glse = None if lse is None else lse[b, :, g * G:(g + 1) * G]
         par = None if inst.parents is None else inst.parents[b]
-        mx, _ = check_output(gout, glse, u, used, bs, inst.scale, w.dtype, parents=par)
-        stats["max_abs"] = max(stats["max_abs"], mx)
+        e = check_output(gout, glse, u, used, bs, inst.scale, w.dtype, parents=par)
+        for key in ("max_abs", "rel", "bound", "lse"):
+            stats[key] = max(stats[key], e.get(key, 0.0))
+        mean_sum += e["mean_abs"]
+        stats["units"] += 1
         sels[(b, g)] = used
+    stats["mean_abs"] = mean_sum / max(stats["units"], 1)
     return sels, stats

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = sv.lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert sv.abi_version() == 2
+    assert sv.abi_version() == 3
 
 
 def test_status_strings():
@@ -152,12 +152,12 @@ def test_select_rejects_bad_budget_and_workspace():
 def test_repr_and_reuse_reject_before_launch():
     lib = sv.lib()
     shape = _shape()
-    assert lib.sv_block_repr(ctypes.byref(shape), None, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE,
-                             FAKE, None) == 1
-    assert lib.sv_block_repr(ctypes.byref(shape), FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE,
-                             FAKE, None) == 2
+    assert lib.sv_block_repr(ctypes.byref(shape), None, FAKE, 4, FAKE, FAKE, None, FAKE, FAKE,
+                             FAKE, FAKE, None) == 1
+    assert lib.sv_block_repr(ctypes.byref(shape), FAKE, FAKE, -1, FAKE, FAKE, None, FAKE, FAKE,
+                             FAKE, FAKE, None) == 2
     assert lib.sv_block_repr(ctypes.byref(_shape(head_dim=32)), FAKE, FAKE, 4, FAKE, FAKE, FAKE,
-                             FAKE, FAKE, FAKE, None) == 3
+                             FAKE, FAKE, FAKE, FAKE, None) == 3
     assert lib.sv_reuse_indices(ctypes.byref(shape), 64, None, FAKE, FAKE, FAKE, None) == 1
     # overlapping source and destination
     assert lib.sv_reuse_indices(ctypes.byref(shape), 64, FAKE, ctypes.c_void_p(0x900000), FAKE,
@@ -204,3 +204,66 @@ def test_split_ranges_balanced_over_k_max():
     for k_max in (64, 100, 1000):
         for s in (3, 7, 10, 15):
             assert sv.attn_num_splits(shape, k_max, s) == min(s, k_max)
+
+
+# ------------------------------------------------------------------ launch plans
+
+def test_plan_query_reports_the_launch():
+    # stack64k shape: 4 x 8 units, 11 splits, 64-token tiles, 32 rows, two workgroups per
+    # CU (64 KB ring), the bounded-wait merge in the launch
+    p = sv.attn_plan(_shape(num_seqs=4), 64, 0)
+    assert p == dict(num_splits=11, workgroups=12 * 32, tile_tokens=64, padded_rows=32,
+                     ring_kb=64, merge_mode=L.MERGE_IN_LAUNCH_WAIT)
+    # qwen128k shape: 2 x 4 units of 128 rows, 128-token tiles, one workgroup per CU
+    q = sv.attn_plan(_shape(num_seqs=2, num_kv_heads=4, num_draft=16, block_size=128), 128, 0)
+    assert (q["tile_tokens"], q["padded_rows"], q["ring_kb"]) == (128, 128, 128)
+    assert q["workgroups"] == (q["num_splits"] + 1) * 8 <= 256
+    assert q["merge_mode"] == L.MERGE_IN_LAUNCH_WAIT
+    # one split: no merge; a grid beyond the device: the last arriver merges; more than
+    # 32 workgroups per unit: the merge kernel
+    assert sv.attn_plan(_shape(num_seqs=4), 64, 1)["merge_mode"] == L.MERGE_NONE
+    big = sv.attn_plan(_shape(num_seqs=8), 64, 16)
+    assert big["workgroups"] == 17 * 64 > 512 and big["merge_mode"] == L.MERGE_IN_LAUNCH_LAST
+    assert sv.attn_plan(_shape(num_seqs=1), 64, 40)["merge_mode"] == L.MERGE_KERNEL
+
+
+def test_plan_query_rejects_bad_arguments():
+    lib = sv.lib()
+    plan = L.AttnPlan()
+    assert lib.sv_attn_plan_query(ctypes.byref(_shape()), 64, 0, None) == 1
+    assert lib.sv_attn_plan_query(ctypes.byref(_shape()), 0, 0, ctypes.byref(plan)) == 2
+    assert lib.sv_attn_plan_query(ctypes.byref(_shape(head_dim=96)), 64, 0,
+                                  ctypes.byref(plan)) == 3
+    assert lib.sv_attn_plan_query(ctypes.byref(_shape()), 64, -1, ctypes.byref(plan)) == 2
+
+
+def _reachable_builds():
+    """Every (dtype, D, tile tokens, padded rows, ring KB) the plan query can return,
+    swept over the supported envelope."""
+    out = set()
+    rows_gt = [(1, 1), (2, 8), (4, 4), (4, 8), (8, 8), (8, 16), (3, 5), (6, 10)]
+    for dtype, dname in ((sv.SV_F32, "fp32"), (sv.SV_BF16, "bf16")):
+        for d in (64, 128):
+            for bs in (32, 64, 128):
+                for g, t in rows_gt:
+                    for b, hkv in ((1, 1), (1, 8), (2, 8), (4, 8), (16, 8)):
+                        for k_max in (1, 8, 64, 512):
+                            shape = _shape(num_seqs=b, num_kv_heads=hkv, num_q_heads=hkv * g,
+                                           num_draft=t, head_dim=d, block_size=bs, dtype=dtype,
+                                           max_blocks_per_seq=1024)
+                            for splits in (0, 1, 2, 7, 20, 31, 1000):
+                                p = sv.attn_plan(shape, k_max, splits)
+                                out.add((dname, d, p["tile_tokens"], p["padded_rows"],
+                                         p["ring_kb"]))
+    return out
+
+
+def test_parity_matrix_launches_every_build():
+    # The GPU parity matrix (tests/cases.py) must launch every attention build the
+    # library can pick, through the separate calls and through the fused entry point.
+    import cases as C
+    universe = _reachable_builds()
+    assert len(universe) >= 30
+    covered = {C.build_key(w, splits, fused) for _, w, splits, fused in C.matrix_cases()}
+    missing = [(b, f) for b in sorted(universe) for f in (False, True) if b + (f,) not in covered]
+    assert not missing, f"builds no parity test launches: {missing}"

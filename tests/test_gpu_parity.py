@@ -15,11 +15,13 @@ import torch
 from block_sparse_speculative_amd import synth
 from block_sparse_speculative_amd.workload import Instance
 
+import cases as C
 import parity as PT
 
 pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS
+SMALL, EDGE, TREES = C.SMALL, C.EDGE, C.TREES
 
 
 def _gpu():
@@ -36,8 +38,9 @@ def _all_units(inst):
     return [(b, g) for b in range(inst.w.num_seqs) for g in range(inst.w.num_kv_heads)]
 
 
-def run_and_check(inst, units=None, layers=None, check_reps=True, scores=False):
-    """Run one pass of `inst` and check the listed units of the listed layers."""
+def run_and_check(inst, units=None, layers=None, check_reps=True, scores=False, case=None):
+    """Run one pass of `inst` and check the listed units of the listed layers; the
+    observed errors are recorded under `case` (default: the workload's name)."""
     n = len(inst.layers)
     layers = list(range(n)) if layers is None else layers
     units = _all_units(inst) if units is None else units
@@ -65,38 +68,13 @@ def run_and_check(inst, units=None, layers=None, check_reps=True, scores=False):
                                             check_reps_too=check_reps and not ly.reuse,
                                             gpu_scores=gscores if (scores and not ly.reuse) else None)
         PT.log(f"  layer {l} ({'reuse' if ly.reuse else 'select'}): {st}")
+        PT.record(f"{case or inst.w.name} L{l}", **st)
         prev = sels
         stats_all.append(st)
     return stats_all
 
 
 # ------------------------------------------------------------------ small workloads
-
-SMALL = {
-    "tiny": W["tiny"],
-    "llama_small": W["llama32k"].with_(num_seqs=2, num_q_heads=8, num_kv_heads=2, ctx=(8192, 6000)),
-    "qwen_small": W["qwen128k"].with_(num_seqs=1, num_q_heads=16, num_kv_heads=2, ctx=(40000,)),
-    "ragged_small": W["ragged"].with_(num_seqs=3, num_q_heads=8, num_kv_heads=2,
-                                      ctx=(4096, 5000, 9000), ctx_range=None),
-    "rows64": W["llama32k"].with_(num_q_heads=16, num_kv_heads=2, ctx=(7000,)),
-    "d64_bs32": W["llama32k"].with_(head_dim=64, block_size=32, num_draft=2, num_q_heads=16,
-                                    num_kv_heads=2, ctx=(3000,), budget=(0, 16, 100, 1, 1)),
-    "fp32_d128": W["tiny"].with_(head_dim=128, block_size=64, ctx=(5000,),
-                                 budget=(0, 12, 0, 1, 1), plant_count=4),
-    "fp32_rows32_bs128": W["tiny"].with_(num_draft=8, block_size=128, ctx=(4500,),
-                                         budget=(0, 8, 0, 1, 1)),
-    # fp32 units of 64 and 128 rows (one workgroup per CU, 32-token tiles)
-    "fp32_rows64_d64": W["tiny"].with_(num_q_heads=16, num_kv_heads=2, num_draft=8,
-                                       ctx=(2500,)),
-    "fp32_rows128_d128": W["tiny"].with_(num_q_heads=16, num_kv_heads=2, num_draft=16,
-                                         head_dim=128, block_size=64, ctx=(3000,),
-                                         budget=(0, 12, 0, 1, 1)),
-    # more than 1024 blocks per row: LDS radix top-k, and the fused call's fallback
-    "long_table": W["llama32k"].with_(num_seqs=1, num_q_heads=8, num_kv_heads=2, block_size=32,
-                                      ctx=(40000,)),
-}
-
-
 @pytest.mark.parametrize("name", list(SMALL))
 @pytest.mark.parametrize("splits", [0, 1, 2, 1000])
 def test_small_workload_all_units(name, splits):
@@ -104,7 +82,7 @@ def test_small_workload_all_units(name, splits):
     PT.log(f"[small] {name} splits={splits}")
     inst = Instance(SMALL[name], seed=11, num_splits=splits, nan_pool=True)
     PT.log(f"  resolved splits={inst.num_splits} k_max={inst.k_max}")
-    run_and_check(inst, scores=(splits == 0))
+    run_and_check(inst, scores=(splits == 0), case=f"small {name} s{splits}")
     del inst
     _free()
 
@@ -117,7 +95,7 @@ def test_small_workload_fused_select_and_attend(name, splits):
     PT.log(f"[fused] {name} splits={splits}")
     w = SMALL[name].with_(num_layers=2, reuse_odd_layers=True)
     a = Instance(w, seed=12, num_splits=splits, nan_pool=True, fused=True)
-    run_and_check(a)
+    run_and_check(a, case=f"fused {name} s{splits}")
     b = Instance(w, seed=12, num_splits=splits, nan_pool=True, fused=False)
     b.step()
     torch.cuda.synchronize()
@@ -125,6 +103,23 @@ def test_small_workload_fused_select_and_attend(name, splits):
         assert torch.equal(la.idx, lb.idx) and torch.equal(la.cnt, lb.cnt)
         assert torch.equal(la.out, lb.out) and torch.equal(la.lse, lb.lse)
     del a, b
+    _free()
+
+
+@pytest.mark.parametrize("case", C.matrix_cases(), ids=lambda c: c[0])
+def test_build_matrix_all_units(case):
+    # every attention build the library can launch (tests/cases.py), checked on every
+    # unit against the oracle; the launch plan must be the build the case stands for
+    _gpu()
+    cid, w, splits, fused = case
+    PT.log(f"[matrix] {cid}")
+    inst = Instance(w, seed=41, num_splits=splits, nan_pool=True, fused=fused)
+    plan = inst.plan
+    PT.log(f"  plan {plan}")
+    key = C.build_key(w, splits, fused)
+    assert (plan["tile_tokens"], plan["padded_rows"], plan["ring_kb"]) == key[2:5]
+    run_and_check(inst, case=cid)
+    del inst
     _free()
 
 
@@ -307,7 +302,7 @@ def test_decode_loop_append_matches_bulk_bit_identical():
         if tail:
             last = phys[full]
             assert torch.equal(pool.k[last][:, :tail], ref.k[last][:, :tail])
-            assert torch.equal(pool.v[last][:, :, :tail], ref.v[last][:, :, :tail])
+            assert torch.equal(pool.v[last][:, :tail], ref.v[last][:, :tail])
 
 
 # ------------------------------------------------------------------ invariances
@@ -362,6 +357,41 @@ def test_merge_tags_on_a_shared_workspace():
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), f"splits {splits}"
 
 
+def _copy_to_high_word(t: torch.Tensor) -> torch.Tensor:
+    """A copy of t in device memory whose address has bit 31 set in its low 32 bits."""
+    nbytes = t.numel() * t.element_size()
+    buf = torch.empty(nbytes + 2 ** 31 + 512, dtype=torch.uint8, device=t.device)
+    base = buf.data_ptr()
+    off = 0 if (base & 0xFFFFFFFF) >= 0x80000000 else 0x80000000 - (base & 0xFFFFFFFF)
+    off = (off + 255) // 256 * 256
+    view = buf[off:off + nbytes].view(t.dtype).view(t.shape)
+    view.copy_(t)
+    assert (view.data_ptr() & 0xFFFFFFFF) >= 0x80000000
+    return view
+
+
+@pytest.mark.parametrize("name", ["llama_small", "tiny", "qwen_small"])
+def test_buffers_whose_address_low_word_has_bit31_set(name):
+    # Regression: the attention kernel forms its DMA base from two 32-bit halves; a low
+    # half with bit 31 set must not spill into the high half. Pools, draft K/V and
+    # queries at such addresses give exactly the results of ordinary allocations.
+    _gpu()
+    from block_sparse_speculative_amd import pipeline as PL
+    inst = Instance(SMALL[name], seed=29)
+    ref = _outputs(inst)
+    for ly in inst.layers:
+        ly.pool = PL.Pool(_copy_to_high_word(ly.pool.k), _copy_to_high_word(ly.pool.v),
+                          _copy_to_high_word(ly.pool.reps))
+        ly.k_draft = _copy_to_high_word(ly.k_draft)
+        ly.v_draft = _copy_to_high_word(ly.v_draft)
+        ly.q = _copy_to_high_word(ly.q)
+    got = _outputs(inst)
+    for x, y in zip(got, ref):
+        assert torch.equal(x, y)
+    del inst
+    _free()
+
+
 def test_paged_and_contiguous_tables_bit_identical():
     _gpu()
     w = SMALL["ragged_small"]
@@ -400,22 +430,106 @@ def test_split_counts_agree_within_tolerance():
         assert (o - outs[0]).abs().max().item() <= 1e-2
 
 
-def test_merge_kernel_path_when_the_grid_exceeds_the_device():
-    # 64 units x 17 workgroups > 512 resident workgroups: the separate merge kernel
+def test_last_arriver_merge_when_the_grid_exceeds_the_device():
+    # 64 units x 17 workgroups > 512 resident workgroups: the last workgroup of each unit
+    # to arrive merges the whole unit inside the launch
     _gpu()
+    from block_sparse_speculative_amd import _lib as L
     w = W["llama32k"].with_(num_seqs=8, ctx=(8192,) * 8)
     inst = Instance(w, seed=23, num_splits=16, fused=True)
-    assert (inst.num_splits + 1) * 64 > 512
-    run_and_check(inst, units=[(0, 0), (3, 5), (7, 7)])
+    assert inst.plan["workgroups"] == 17 * 64 > 512
+    assert inst.plan["merge_mode"] == L.MERGE_IN_LAUNCH_LAST
+    run_and_check(inst, units=[(0, 0), (3, 5), (7, 7), (5, 2)], case="merge last-arriver")
+
+
+def test_merge_kernel_when_a_unit_has_more_than_32_workgroups():
+    _gpu()
+    from block_sparse_speculative_amd import _lib as L
+    w = W["llama32k"].with_(num_seqs=1, num_q_heads=8, num_kv_heads=2, ctx=(8192,))
+    inst = Instance(w, seed=25, num_splits=40, fused=True)
+    assert inst.plan["merge_mode"] == L.MERGE_KERNEL
+    run_and_check(inst, case="merge kernel")
 
 
 def test_in_kernel_merge_at_full_residency():
     # 32 units x 16 workgroups = 512 workgroups, two per CU: every one resident
     _gpu()
+    from block_sparse_speculative_amd import _lib as L
     w = W["stack64k"].with_(num_layers=2, ctx=(8192,) * 4)
     inst = Instance(w, seed=24, num_splits=15, fused=True)
-    assert (inst.num_splits + 1) * 32 == 512
-    run_and_check(inst, units=[(0, 0), (1, 3), (3, 7)])
+    assert inst.plan["workgroups"] == 512 and inst.plan["ring_kb"] == 64
+    assert inst.plan["merge_mode"] == L.MERGE_IN_LAUNCH_WAIT
+    run_and_check(inst, units=[(0, 0), (1, 3), (3, 7)], case="merge wait, full residency")
+
+
+def test_merge_with_other_kernels_holding_the_device():
+    # The in-launch merge must not depend on the whole grid being resident: here long
+    # independent matrix products run on a second stream (same priority) while the
+    # attention runs, so some of a unit's workgroups may start only after others have
+    # finished their stream. Each workgroup waits for its siblings at most a bounded
+    # time, then hands its slice to the last one to arrive. Outputs must match the
+    # oracle exactly as on an idle device, with no NaN.
+    _gpu()
+    from block_sparse_speculative_amd import _lib as L
+    w = W["stack64k"].with_(num_layers=2, ctx=(8192,) * 4)
+    inst = Instance(w, seed=26, fused=True)
+    assert inst.plan["merge_mode"] == L.MERGE_IN_LAUNCH_WAIT
+    inst.step()
+    torch.cuda.synchronize()
+    idle = [(ly.out.clone(), ly.lse.clone()) for ly in inst.layers]
+    a = torch.randn(8192, 8192, device=inst.device, dtype=torch.bfloat16)
+    bm = torch.randn(8192, 8192, device=inst.device, dtype=torch.bfloat16)
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        for ly in inst.layers:
+            ly.out.fill_(float("nan"))
+            ly.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            for _ in range(6):
+                a = (a @ bm) * (1.0 / 128.0)
+        inst.step()                     # on the current stream, concurrently
+        torch.cuda.synchronize()
+        for ly, (o, l_) in zip(inst.layers, idle):
+            assert torch.isfinite(ly.out.float()).all() and torch.isfinite(ly.lse).all()
+            assert torch.equal(ly.out, o) and torch.equal(ly.lse, l_), f"replay {rep}"
+    run_and_check(inst, units=[(0, 0), (1, 3), (2, 5), (3, 7)], case="merge under load")
+
+
+def test_workspace_grown_to_more_units_after_zero_fill():
+    # A workspace used by calls of 2 units and then (after the documented zero-fill) of
+    # 4 units, with a one-split call in between, gives exactly what fresh workspaces give.
+    _gpu()
+    from block_sparse_speculative_amd import _lib as L
+    from block_sparse_speculative_amd import pipeline as PL
+    small = W["llama32k"].with_(num_seqs=1, num_q_heads=8, num_kv_heads=2, ctx=(8192,))
+    big = small.with_(num_seqs=2, ctx=(8192, 7000))
+    insts = [Instance(small, seed=27, fused=True), Instance(big, seed=28, fused=True)]
+    nbytes = max(L.select_and_attend_workspace_bytes(i.shape, i.k_max, s)
+                 for i in insts for s in (0, 1, 3))
+    shared = torch.zeros(nbytes, dtype=torch.uint8, device=insts[0].device)
+
+    def call(inst, splits, ws):
+        ly = inst.layers[0]
+        idx, cnt = torch.empty_like(ly.idx), torch.empty_like(ly.cnt)
+        out, lse = torch.empty_like(ly.out), torch.empty_like(ly.lse)
+        L.select_and_attend(inst.shape, inst.budget, ly.q, ly.pool.reps, ly.k_draft, ly.v_draft,
+                            ly.pool.k, ly.pool.v, inst.table, inst.ctx, inst.k_max, inst.scale,
+                            idx, cnt, out, lse=lse, ws=ws, num_splits=splits)
+        return idx, out, lse
+
+    seq = [(0, 3), (0, 1), (0, 0), (1, 3), (1, 1), (1, 0), (1, 3)]
+    for i, (which, splits) in enumerate(seq):
+        inst = insts[which]
+        if i == 3:
+            shared.zero_()             # more units than before: zero-fill as documented
+        got = call(inst, splits, shared)
+        fresh = torch.zeros(L.select_and_attend_workspace_bytes(inst.shape, inst.k_max, splits),
+                            dtype=torch.uint8, device=inst.device)
+        want = call(inst, splits, fresh)
+        torch.cuda.synchronize()
+        for x, y in zip(got, want):
+            assert torch.equal(x, y), f"call {i}"
 
 
 def test_stack_with_reuse_small():
@@ -431,20 +545,19 @@ def test_full_llama32k_all_units():
     _gpu()
     PT.log("[full] llama32k")
     inst = Instance(W["llama32k"], seed=1, fused=True)
-    run_and_check(inst)
+    run_and_check(inst, case="full llama32k")
     del inst
     _free()
 
 
-def test_full_ragged_sampled_units():
+def test_full_ragged_all_units():
+    # all 16 x 8 units of the ragged batch (contexts 4K-64K, paged), bench launch
+    # configuration
     _gpu()
     PT.log("[full] ragged")
     inst = Instance(W["ragged"], seed=2, fused=True)
-    lens = inst.ctx_lens
-    bs = [int(np.argmin(lens)), int(np.argmax(lens)), 5, 11]
-    units = sorted({(b, g) for b, g in zip(bs, [0, 7, 3, 5])})
-    PT.log(f"  ctx_lens={lens} units={units}")
-    run_and_check(inst, units=units)
+    PT.log(f"  ctx_lens={inst.ctx_lens} plan={inst.plan}")
+    run_and_check(inst, case="full ragged")
     del inst
     _free()
 
@@ -453,16 +566,21 @@ def test_full_qwen128k_all_units():
     _gpu()
     PT.log("[full] qwen128k")
     inst = Instance(W["qwen128k"], seed=4, fused=True)
-    run_and_check(inst, check_reps=False)
+    PT.log(f"  plan={inst.plan}")
+    run_and_check(inst, check_reps=False, case="full qwen128k")
     del inst
     _free()
 
 
-def test_full_stack64k_sampled_layers_and_units():
+@pytest.mark.parametrize("first,count", [(0, 4), (30, 2)])
+def test_full_stack64k_layers_all_units(first, count):
+    # all 4 x 8 units of stack64k layers 0-3 and 30-31 (select, reuse, select, reuse),
+    # bench launch configuration (the layers' inputs are those of the 32-layer stack)
     _gpu()
-    PT.log("[full] stack64k (32 layers)")
-    inst = Instance(W["stack64k"], seed=3, fused=True)
-    run_and_check(inst, units=[(0, 0), (3, 7), (2, 4)], layers=[0, 1, 30, 31], check_reps=False)
+    PT.log(f"[full] stack64k layers {first}..{first + count - 1}")
+    inst = Instance(W["stack64k"], seed=3, fused=True, num_layers=count, layer_offset=first)
+    PT.log(f"  plan={inst.plan}")
+    run_and_check(inst, check_reps=False, case=f"full stack64k from L{first}")
     del inst
     _free()
 
