@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <string>
 
+#include "api_internal.h"
 #include "internal.h"
 #include "sv.h"
 
@@ -161,24 +162,40 @@ size_t merge_lines_bytes(const sv_shape* s) {
   return align_up(units * sv::kTicketStride * sizeof(uint32_t));
 }
 
-// Attention workspace: [merge lines: units x 256 B][partial O][partial (m, l)]; nothing
-// with one split.
-size_t attn_ws_layout(const sv_shape* s, int splits, size_t* o_off, size_t* ml_off) {
-  size_t o_dummy, ml_dummy;
-  if (!o_off) o_off = &o_dummy;
-  if (!ml_off) ml_off = &ml_dummy;
-  if (splits <= 1) {
-    *o_off = *ml_off = 0;
-    return 0;
-  }
+// Region after the merge lines: [partial O][partial (m, l)] when there is more than one
+// split, then (fused calls only) the block scores. Offsets are relative to its start.
+struct RestLayout {
+  size_t o_off, ml_off, scores_off, attn_end, fused_end;
+};
+
+RestLayout rest_layout(const sv_shape* s, int splits) {
+  RestLayout r{};
   const size_t rows = static_cast<size_t>(s->num_draft) * (s->num_q_heads / s->num_kv_heads);
   const size_t units = static_cast<size_t>(s->num_seqs) * s->num_kv_heads;
-  const size_t parts = static_cast<size_t>(splits) + 1;   // + the draft-only split
-  *o_off = merge_lines_bytes(s);
-  *ml_off = *o_off + align_up(units * parts * rows * s->head_dim * sizeof(float));
-  return *ml_off + align_up(units * parts * rows * 2 * sizeof(float));
+  if (splits > 1) {
+    const size_t parts = static_cast<size_t>(splits) + 1;   // + the draft-only split
+    r.o_off = 0;
+    r.ml_off = align_up(units * parts * rows * s->head_dim * sizeof(float));
+    r.attn_end = r.ml_off + align_up(units * parts * rows * 2 * sizeof(float));
+  }
+  r.scores_off = r.attn_end;
+  size_t sc_off;
+  r.fused_end = r.scores_off + select_ws_layout(s, &sc_off);
+  return r;
 }
 
+// Attention workspace: [merge lines: units x 256 B][partial O][partial (m, l)]; nothing
+// with one split.
+size_t attn_ws_bytes(const sv_shape* s, int splits) {
+  return splits <= 1 ? 0 : merge_lines_bytes(s) + rest_layout(s, splits).attn_end;
+}
+
+// Workspace of sv_select_and_attend: [merge lines][partials][scores]. The merge lines are
+// reserved even with one split, so the scores never land on them whatever split
+// counts calls on one workspace use.
+size_t fused_ws_bytes(const sv_shape* s, int splits) {
+  return merge_lines_bytes(s) + rest_layout(s, splits).fused_end;
+}
 
 sv::SelectParams select_params(const sv_shape* shape, const sv_budget* budget, const void* q,
                                const float* repr_pool, const int32_t* block_table,
@@ -210,16 +227,16 @@ sv::SelectParams select_params(const sv_shape* shape, const sv_budget* budget, c
   return p;
 }
 
-// Attention parameters with the workspace carved as attn_ws_layout says (ws may
-// be NULL when ws_need is 0); idx / cnt / scores are set by the caller.
+// Attention parameters; `lines` and `rest` are the merge lines and the region after
+// them (both unused with one split).
 sv::AttnParams attn_params(const sv_shape* shape, const void* q, const void* k_draft,
                            const void* v_draft, const void* k_pool, const void* v_pool,
                            const int32_t* block_table, const int32_t* ctx_lens, int32_t k_max,
-                           float scale, int splits, void* out, float* lse, void* ws,
-                           size_t ws_need) {
-  size_t o_off, ml_off;
-  attn_ws_layout(shape, splits, &o_off, &ml_off);
-  char* w = static_cast<char*>(ws);
+                           float scale, int splits, void* out, float* lse, void* lines,
+                           void* rest) {
+  const RestLayout rl = rest_layout(shape, splits);
+  char* w = static_cast<char*>(rest);
+  const bool parts = splits > 1;
   sv::AttnParams p{};
   p.q = q;
   p.k_draft = k_draft;
@@ -230,8 +247,8 @@ sv::AttnParams attn_params(const sv_shape* shape, const void* q, const void* k_d
   p.ctx_lens = ctx_lens;
   p.out = out;
   p.lse = lse;
-  p.part_o = ws_need ? reinterpret_cast<float*>(w + o_off) : nullptr;
-  p.part_ml = ws_need ? reinterpret_cast<float*>(w + ml_off) : nullptr;
+  p.part_o = parts ? reinterpret_cast<float*>(w + rl.o_off) : nullptr;
+  p.part_ml = parts ? reinterpret_cast<float*>(w + rl.ml_off) : nullptr;
   p.B = shape->num_seqs;
   p.Hq = shape->num_q_heads;
   p.Hkv = shape->num_kv_heads;
@@ -245,7 +262,7 @@ sv::AttnParams attn_params(const sv_shape* shape, const void* q, const void* k_d
   p.S = splits;
   p.R = shape->num_draft * p.G;
   p.xcd_group = sv::xcd_groupable(p.B * p.Hkv) ? 1 : 0;
-  p.tickets = ws_need ? reinterpret_cast<uint32_t*>(w) : nullptr;
+  p.tickets = parts ? static_cast<uint32_t*>(lines) : nullptr;
   const DeviceInfo dev = device_info();
   p.merge = sv::attn_merge_mode(splits, p.B * p.Hkv, p.R, shape->dtype == SV_BF16, dev.cus);
   p.merge_wait_ticks = static_cast<uint32_t>(static_cast<int64_t>(dev.wall_khz) *
@@ -254,18 +271,87 @@ sv::AttnParams attn_params(const sv_shape* shape, const void* q, const void* k_d
   return p;
 }
 
-// Workspace of sv_select_and_attend: [attention workspace][scores]. The merge lines are
-// reserved even with one split, so the scores never land on them whatever split
-// counts calls on one workspace use.
-size_t fused_ws_layout(const sv_shape* s, int splits, size_t* scores_off) {
-  const size_t attn = attn_ws_layout(s, splits, nullptr, nullptr);
-  const size_t lines = merge_lines_bytes(s);
-  *scores_off = align_up(attn > lines ? attn : lines);
-  size_t sc_off;
-  return *scores_off + select_ws_layout(s, &sc_off);
+}  // namespace
+
+namespace sv {
+
+sv_status fail_status(sv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
 }
 
-}  // namespace
+sv_status check_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
+                                  const float* repr_pool, const void* k_draft,
+                                  const void* v_draft, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* ctx_lens,
+                                  int32_t k_max, float scale, int32_t num_splits, int32_t* idx,
+                                  int32_t* cnt, void* out, const char* what) {
+  if (sv_status st = check_shape(shape, what)) return st;
+  if (sv_status st = check_budget(budget, what)) return st;
+  if (sv_status st = check_kmax(shape, k_max, what)) return st;
+  if (num_splits < 0) return fail(SV_ERR_BAD_SHAPE, "%s: num_splits < 0", what);
+  if (!(scale > 0.0f) || scale == __builtin_inff())
+    return fail(SV_ERR_BAD_SHAPE, "%s: scale must be finite and positive", what);
+  if (shape->num_seqs == 0) return SV_OK;
+  if (!q || !repr_pool || !k_draft || !v_draft || !k_pool || !v_pool || !block_table ||
+      !ctx_lens || !idx || !cnt || !out)
+    return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  return SV_OK;
+}
+
+int resolve_splits_checked(const sv_shape* shape, int32_t k_max, int32_t num_splits) {
+  return resolve_splits(shape, k_max, num_splits);
+}
+
+size_t fused_rest_bytes(const sv_shape* shape, int splits) {
+  return rest_layout(shape, splits).fused_end;
+}
+
+sv_status select_and_attend_into(const sv_shape* shape, const sv_budget* budget, const void* q,
+                                 const float* repr_pool, const void* k_draft,
+                                 const void* v_draft, const int32_t* draft_mask,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const int32_t* ctx_lens,
+                                 int32_t k_max, float scale, int splits, int32_t* idx,
+                                 int32_t* cnt, void* out, float* lse, void* lines, void* rest,
+                                 hipStream_t st, const char* what) {
+  const bool bf16 = shape->dtype == SV_BF16;
+  float* scores = reinterpret_cast<float*>(static_cast<char*>(rest) +
+                                           rest_layout(shape, splits).scores_off);
+  SelectParams sp = select_params(shape, budget, q, repr_pool, block_table, ctx_lens, k_max, idx,
+                                  cnt);
+  sp.scores = scores;
+  sp.scores_requested = 0;
+  AttnParams ap = attn_params(shape, q, k_draft, v_draft, k_pool, v_pool, block_table, ctx_lens,
+                              k_max, scale, splits, out, lse, lines, rest);
+  ap.idx = idx;
+  ap.cnt = cnt;
+  ap.draft_mask = draft_mask;
+  hipError_t e = launch_score(sp, bf16, st);
+  if (e != hipSuccess) return from_hip(e, what);
+  if (shape->max_blocks_per_seq <= kWaveTopkMaxBlocks) {
+    // Budget + top-k run inside the attention workgroups.
+    ap.scores = scores;
+    ap.idx_out = idx;
+    ap.cnt_out = cnt;
+    ap.dense_ctx = budget->dense_ctx_tokens;
+    ap.min_blocks = budget->min_blocks;
+    ap.frac_per_mille = budget->frac_per_mille;
+    ap.keep_first = budget->keep_first;
+    ap.keep_last = budget->keep_last;
+  } else {
+    e = launch_topk(sp, st);
+    if (e != hipSuccess) return from_hip(e, what);
+  }
+  return from_hip(launch_attn(ap, bf16, st), what);
+}
+
+}  // namespace sv
 
 extern "C" {
 
@@ -363,8 +449,7 @@ int32_t sv_attn_num_splits(const sv_shape* shape, int32_t k_max, int32_t num_spl
 size_t sv_attn_workspace_bytes(const sv_shape* shape, int32_t k_max, int32_t num_splits) {
   if (check_shape(shape, "sv_attn_workspace_bytes") != SV_OK) return 0;
   if (check_kmax(shape, k_max, "sv_attn_workspace_bytes") != SV_OK) return 0;
-  size_t o_off, ml_off;
-  return attn_ws_layout(shape, resolve_splits(shape, k_max, num_splits), &o_off, &ml_off);
+  return attn_ws_bytes(shape, resolve_splits(shape, k_max, num_splits));
 }
 
 sv_status sv_attn_plan_query(const sv_shape* shape, int32_t k_max, int32_t num_splits,
@@ -410,12 +495,14 @@ sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void
       !cnt || !out)
     return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
   const int splits = resolve_splits(shape, k_max, num_splits);
-  const size_t need = attn_ws_layout(shape, splits, nullptr, nullptr);
+  const size_t need = attn_ws_bytes(shape, splits);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
                 ws ? ws_bytes : static_cast<size_t>(0));
+  char* w = static_cast<char*>(ws);
   sv::AttnParams p = attn_params(shape, q, k_draft, v_draft, k_pool, v_pool, block_table,
-                                 ctx_lens, k_max, scale, splits, out, lse, ws, need);
+                                 ctx_lens, k_max, scale, splits, out, lse, w,
+                                 need ? w + merge_lines_bytes(shape) : nullptr);
   p.idx = idx;
   p.cnt = cnt;
   p.draft_mask = draft_mask;
@@ -427,8 +514,7 @@ size_t sv_select_and_attend_workspace_bytes(const sv_shape* shape, int32_t k_max
                                             int32_t num_splits) {
   if (check_shape(shape, "sv_select_and_attend_workspace_bytes") != SV_OK) return 0;
   if (check_kmax(shape, k_max, "sv_select_and_attend_workspace_bytes") != SV_OK) return 0;
-  size_t scores_off;
-  return fused_ws_layout(shape, resolve_splits(shape, k_max, num_splits), &scores_off);
+  return fused_ws_bytes(shape, resolve_splits(shape, k_max, num_splits));
 }
 
 sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
@@ -439,53 +525,21 @@ sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, c
                                int32_t* cnt, void* out, float* lse, void* ws, size_t ws_bytes,
                                void* stream) {
   const char* what = "sv_select_and_attend";
-  if (sv_status st = check_shape(shape, what)) return st;
-  if (sv_status st = check_budget(budget, what)) return st;
-  if (sv_status st = check_kmax(shape, k_max, what)) return st;
-  if (num_splits < 0) return fail(SV_ERR_BAD_SHAPE, "%s: num_splits < 0", what);
-  if (!(scale > 0.0f) || scale == __builtin_inff())
-    return fail(SV_ERR_BAD_SHAPE, "%s: scale must be finite and positive", what);
+  if (sv_status st = sv::check_select_and_attend(shape, budget, q, repr_pool, k_draft, v_draft,
+                                                 k_pool, v_pool, block_table, ctx_lens, k_max,
+                                                 scale, num_splits, idx, cnt, out, what))
+    return st;
   if (shape->num_seqs == 0) return ok();
-  if (!q || !repr_pool || !k_draft || !v_draft || !k_pool || !v_pool || !block_table ||
-      !ctx_lens || !idx || !cnt || !out)
-    return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
   const int splits = resolve_splits(shape, k_max, num_splits);
-  size_t scores_off;
-  const size_t need = fused_ws_layout(shape, splits, &scores_off);
+  const size_t need = fused_ws_bytes(shape, splits);
   if (!ws || ws_bytes < need)
     return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
                 ws ? ws_bytes : static_cast<size_t>(0));
-  const bool bf16 = shape->dtype == SV_BF16;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  float* scores = reinterpret_cast<float*>(w + scores_off);
-  sv::SelectParams sp = select_params(shape, budget, q, repr_pool, block_table, ctx_lens, k_max,
-                                      idx, cnt);
-  sp.scores = scores;
-  sp.scores_requested = 0;
-  const size_t attn_need = attn_ws_layout(shape, splits, nullptr, nullptr);
-  sv::AttnParams ap = attn_params(shape, q, k_draft, v_draft, k_pool, v_pool, block_table,
-                                  ctx_lens, k_max, scale, splits, out, lse, ws, attn_need);
-  ap.idx = idx;
-  ap.cnt = cnt;
-  ap.draft_mask = draft_mask;
-  hipError_t e = sv::launch_score(sp, bf16, st);
-  if (e != hipSuccess) return from_hip(e, what);
-  if (shape->max_blocks_per_seq <= sv::kWaveTopkMaxBlocks) {
-    // Budget + top-k run inside the attention workgroups.
-    ap.scores = scores;
-    ap.idx_out = idx;
-    ap.cnt_out = cnt;
-    ap.dense_ctx = budget->dense_ctx_tokens;
-    ap.min_blocks = budget->min_blocks;
-    ap.frac_per_mille = budget->frac_per_mille;
-    ap.keep_first = budget->keep_first;
-    ap.keep_last = budget->keep_last;
-  } else {
-    e = sv::launch_topk(sp, st);
-    if (e != hipSuccess) return from_hip(e, what);
-  }
-  return from_hip(sv::launch_attn(ap, bf16, st), what);
+  return sv::select_and_attend_into(shape, budget, q, repr_pool, k_draft, v_draft, draft_mask,
+                                    k_pool, v_pool, block_table, ctx_lens, k_max, scale, splits,
+                                    idx, cnt, out, lse, w, w + merge_lines_bytes(shape),
+                                    static_cast<hipStream_t>(stream), what);
 }
 
 sv_status sv_reuse_indices(const sv_shape* shape, int32_t k_max, const int32_t* prev_idx,
