@@ -81,6 +81,9 @@ _SIG = [
     ("sv_select_and_attend", _I, [ctypes.POINTER(Shape), ctypes.POINTER(Budget), _P, _P, _P, _P,
                                   _P, _P, _P, _P, _P, _I, ctypes.c_float, _I, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
+    ("sv_select_and_attend_static", _I, [ctypes.POINTER(Shape), ctypes.POINTER(Budget), _P, _P,
+                                         _P, _P, _P, _P, _P, _P, _P, _I, ctypes.c_float, _I, _P,
+                                         _P, _P, _P, _P]),
     ("sv_reuse_indices", _I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P]),
 ]
 EXPORTS = tuple(name for name, _, _ in _SIG)
@@ -287,6 +290,41 @@ def select_and_attend(shape: Shape, budget: Budget, q, repr_pool, k_draft, v_dra
         _ptr(v_draft), _ptr(draft_mask), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(ctx_lens), int(k_max),
         float(scale), int(num_splits), _ptr(idx), _ptr(cnt), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream()))
+
+
+STATIC_SCRATCH_BYTES = 32 << 20     # SV_STATIC_SCRATCH_BYTES
+STATIC_SCRATCH_UNITS = 2048         # SV_STATIC_SCRATCH_UNITS
+
+
+def select_and_attend_static(shape: Shape, budget: Budget, q, repr_pool, k_draft, v_draft,
+                             k_pool, v_pool, block_table, ctx_lens, k_max: int, scale: float,
+                             idx, cnt, out, lse=None, num_splits: int = 0, draft_mask=None):
+    """sv_select_and_attend_static: sv_select_and_attend without a workspace (the library's
+    static per-device scratch; allocates nothing)."""
+    B, Hq, Hkv, D, T = (shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim,
+                        shape.num_draft)
+    e = _elem(shape)
+    P, bs = shape.num_phys_blocks, shape.block_size
+    _dev(q, "q", e, (B, T, Hq, D))
+    _dev(repr_pool, "repr_pool", torch.float32, (P, Hkv, D))
+    _dev(k_draft, "k_draft", e, (B, T, Hkv, D))
+    _dev(v_draft, "v_draft", e, (B, T, Hkv, D))
+    _dev(k_pool, "k_pool", e, (P, Hkv, bs, D))
+    _dev(v_pool, "v_pool", e, (P, Hkv, bs, D))
+    _dev(block_table, "block_table", torch.int32, (B, shape.max_blocks_per_seq))
+    _dev(ctx_lens, "ctx_lens", torch.int32, (B,))
+    _dev(idx, "idx", torch.int32, (B, Hkv, k_max))
+    _dev(cnt, "cnt", torch.int32, (B, Hkv))
+    _dev(out, "out", e, (B, T, Hq, D))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, T, Hq))
+    if draft_mask is not None:
+        _dev(draft_mask, "draft_mask", torch.int32, (B, T))
+    _check(lib().sv_select_and_attend_static(
+        ctypes.byref(shape), ctypes.byref(budget), _ptr(q), _ptr(repr_pool), _ptr(k_draft),
+        _ptr(v_draft), _ptr(draft_mask), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        _ptr(ctx_lens), int(k_max), float(scale), int(num_splits), _ptr(idx), _ptr(cnt),
+        _ptr(out), _ptr(lse), _stream()))
 
 
 def reuse_indices(shape: Shape, k_max: int, prev_idx, prev_cnt, idx, cnt):

@@ -270,6 +270,30 @@ sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, c
                                int32_t* cnt, void* out, float* lse, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* Size of the device array sv_select_and_attend_static works in (one per device), and
+ * the most (sequence, KV head) units a call of it may have. */
+#define SV_STATIC_SCRATCH_BYTES (32u << 20)
+#define SV_STATIC_SCRATCH_UNITS 2048
+
+/* sv_select_and_attend for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * results and launches as sv_select_and_attend, minus the workspace: the partials,
+ * merge lines and block scores live in a fixed array of SV_STATIC_SCRATCH_BYTES in
+ * device memory that the library holds on each device it runs on until the process
+ * ends. The call allocates nothing. It returns SV_ERR_WORKSPACE (nothing launched) when
+ * num_seqs * num_kv_heads exceeds SV_STATIC_SCRATCH_UNITS or the partials and scores of
+ * the call do not fit (use sv_select_and_attend then). Every call on a device shares
+ * that device's array, so calls that may overlap on one device (other streams or
+ * threads) race and must not be issued; consecutive calls on one stream are fine. */
+sv_status sv_select_and_attend_static(const sv_shape* shape, const sv_budget* budget,
+                                      const void* q, const float* repr_pool, const void* k_draft,
+                                      const void* v_draft, const int32_t* draft_mask,
+                                      const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      int32_t k_max, float scale, int32_t num_splits,
+                                      int32_t* idx, int32_t* cnt, void* out, float* lse,
+                                      void* stream);
+
 /* Inter-layer retrieval reuse (tutorial page, "Core technique 1": some layers take
  * the previous layer's retrieval result instead of selecting again; sciencestack
  * abstract: inter-layer retrieval reuse). Copies prev_idx [B, Hkv, k_max] and

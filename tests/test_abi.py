@@ -267,3 +267,23 @@ def test_parity_matrix_launches_every_build():
     covered = {C.build_key(w, splits, fused) for _, w, splits, fused in C.matrix_cases()}
     missing = [(b, f) for b in sorted(universe) for f in (False, True) if b + (f,) not in covered]
     assert not missing, f"builds no parity test launches: {missing}"
+
+
+def test_static_entry_point_rejects_what_its_scratch_cannot_hold():
+    # validated on the host before anything touches a device
+    lib = sv.lib()
+    good = ctypes.byref(sv.make_budget(4096, 64, 50))
+
+    def call(shape, k_max=64, splits=0):
+        return lib.sv_select_and_attend_static(ctypes.byref(shape), good, FAKE, FAKE, FAKE, FAKE,
+                                               None, FAKE, FAKE, FAKE, FAKE, k_max, 0.1, splits,
+                                               FAKE, FAKE, FAKE, None, None)
+
+    assert call(_shape(num_seqs=257)) == 4                     # 2056 units > 2048
+    assert b"units" in lib.sv_last_error()
+    # 128 units x 32 workgroups x 128 rows x 128 dims of fp32 partials: 64 MiB > 32 MiB
+    assert call(_shape(num_seqs=32, num_kv_heads=4, num_q_heads=32, num_draft=16),
+                k_max=256, splits=31) == 4
+    assert b"bytes" in lib.sv_last_error()
+    assert call(_shape(head_dim=96)) == 3
+    assert call(_shape(), k_max=0) == 2
