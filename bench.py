@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--launch-curve", action="store_true",
                     help="also time the attention entry point against the number of selected "
                          "blocks per unit (fixed cost and streaming rate of one launch)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the qwen128k block that follows the headline workload")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -117,7 +119,8 @@ def cpu_baseline(inst, budget_s: float):
     dense, mn, frac, kf, kl = w.budget
     timed, rows, units_done = 0.0, 0, 0
     done = []                              # (sequence, layers) covered
-    with threadpool_limits(limits=1):
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
         for b in range(w.num_seqs):
             ctx = inst.ctx_lens[b]
             prev = None
@@ -162,11 +165,12 @@ def cpu_baseline(inst, budget_s: float):
     return {
         "value": rows / timed,
         "unit": "draft-token-heads/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": (f"{desc} of {len(inst.layers)} layers, all {w.num_kv_heads} KV heads: "
-                   f"{units_done} units, {rows} draft-token-heads, {timed:.1f} s single-threaded "
-                   f"numpy fp64 (scores, budget, top-k, attention; representatives precomputed)"),
+                   f"{units_done} units, {rows} draft-token-heads, {timed:.1f} s of numpy fp64 "
+                   f"with BLAS on {cores} host threads (scores, budget, top-k, attention; "
+                   f"representatives precomputed)"),
     }
 
 
@@ -322,6 +326,162 @@ def fit_launch_line(points, k_min: int):
     return my - slope * mx, ((1e-3 / slope) if slope > 0 else None)
 
 
+def build_instances(w, args, reps_total: int, progress=None):
+    from block_sparse_speculative_amd.workload import Instance
+    return [Instance(w, seed=args.seed + r, num_splits=args.num_splits, with_lse=False,
+                     progress=progress, fused=not args.separate) for r in range(reps_total)]
+
+
+def capture(fn):
+    """A HIP graph of fn() (one eager warm-up on a side stream first)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
+
+
+def event_time_us(replay, reps: int) -> float:
+    """Average time of one replay(), from HIP events on the current stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    replay()
+    stream.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        replay()
+    ev1.record(stream)
+    ev1.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / reps
+
+
+def measure(w, args, steps: int, warmup: int, label: str):
+    """One pass of the hot path over the workload, graph-replayed `steps` times after
+    `warmup` replays (resident instances rotated past the last-level cache), and the
+    attention launch alone. Returns (instances, figures)."""
+    import torch
+    from block_sparse_speculative_amd import synth
+    from block_sparse_speculative_amd import workload as WL
+
+    bytes_per_pass = WL.algorithmic_bytes(w, synth.context_lengths(w, args.seed), w.num_layers)
+    # Rotate resident copies so one rotation touches more than 2 x 256 MB of selected
+    # data and representatives (the MI355X last-level cache).
+    reps_total = args.instances or max(1, -(-2 * 256 * 2 ** 20 // bytes_per_pass))
+    print(f"[bench] {label} {w.name}: {bytes_per_pass / 1e6:.1f} MB algorithmic per pass, "
+          f"{reps_total} resident instance(s)", file=sys.stderr, flush=True)
+
+    def progress(done, total):
+        if done == total or done % 8 == 0:
+            print(f"[bench]   built layer {done}/{total}", file=sys.stderr, flush=True)
+
+    insts = build_instances(w, args, reps_total, progress)
+    inst0 = insts[0]
+    torch.cuda.synchronize()
+
+    def step():
+        for it in insts:
+            it.step()
+
+    use_graph = not args.no_graph
+    run = capture(step).replay if use_graph else step
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s_per_pass = wall / (steps * reps_total)      # the graph covers reps_total passes
+
+    # ---- roofline of the attention entry point: a graph of only the attention calls
+    # of every layer (indices from the passes above), replayed between HIP events on the
+    # stream it runs on
+    def attend_all():
+        for it in insts:
+            for l in range(len(it.layers)):
+                it.attend(l)
+
+    g_attn = capture(attend_all)
+    attn_us = event_time_us(g_attn.replay, max(3, steps)) / (reps_total * len(inst0.layers))
+    elem = 4 if w.dtype == "fp32" else 2
+    kv_bytes_per_launch = (inst0.selected_tokens() // len(inst0.layers)) * w.head_dim * 2 * elem
+    achieved = kv_bytes_per_launch / (attn_us * 1e-6) / 1e9
+    fig = dict(s_per_pass=s_per_pass, units=inst0.units(), bytes_per_pass=bytes_per_pass,
+               attn_us=attn_us, kv_bytes_per_launch=kv_bytes_per_launch, achieved=achieved,
+               reps_total=reps_total, graph=use_graph)
+    return insts, fig
+
+
+def full_verification_schedule(inst, sparse_pass_us: float, period: int, reps: int):
+    """Periodic full verification: every `period`-th verification pass attends over
+    every block on every layer (through the same attention entry point, no selection),
+    the others are the sparse pass. Times one full pass (graph-replayed, HIP events) and
+    reports the schedule's mean pass time."""
+    import torch
+    from block_sparse_speculative_amd import _lib as L
+    from block_sparse_speculative_amd import pipeline as PL
+
+    w = inst.w
+    B, Hkv = w.num_seqs, w.num_kv_heads
+    nbs = [-(-c // w.block_size) for c in inst.ctx_lens]
+    k_max = max(nbs)
+    idx = torch.full((B, Hkv, k_max), -1, dtype=torch.int32)
+    for b, n in enumerate(nbs):
+        idx[b, :, :n] = torch.arange(n, dtype=torch.int32)
+    idx = idx.to(inst.device)
+    cnt = torch.tensor(nbs, dtype=torch.int32)[:, None].expand(B, Hkv).contiguous().to(inst.device)
+    ws = PL.Workspaces(inst.shape, k_max, 0, inst.device)
+    outs = [torch.empty_like(ly.out) for ly in inst.layers]
+
+    def full_pass():
+        for ly, out in zip(inst.layers, outs):
+            L.sparse_verify_attn(inst.shape, ly.q, ly.k_draft, ly.v_draft, ly.pool.k, ly.pool.v,
+                                 inst.table, inst.ctx, idx, cnt, k_max, inst.scale, out,
+                                 ws=ws.attn, draft_mask=inst.draft_mask)
+
+    full_us = event_time_us(capture(full_pass).replay, reps)
+    mean_us = ((period - 1) * sparse_pass_us + full_us) / period
+    return {"period": period, "full_pass_us": full_us, "sparse_pass_us": sparse_pass_us,
+            "mean_pass_us": mean_us, "full_over_sparse": full_us / sparse_pass_us,
+            "mean_over_sparse": mean_us / sparse_pass_us,
+            "what": "one full verification (every block, every layer) per period passes; the "
+                    "others sparse"}
+
+
+def decode_append(inst, reps: int):
+    """One decode step's KV append on every layer: sv_block_repr writing T tokens per
+    sequence (the last T positions of each context, rewritten in place with ctx_after =
+    the context, so the touched blocks are full) and re-deriving the representatives of
+    the blocks they land in. Graph-replayed, HIP events."""
+    import torch
+    from block_sparse_speculative_amd import pipeline as PL
+
+    w = inst.w
+    B, T = w.num_seqs, w.num_draft
+    dev = inst.device
+    ctx = torch.tensor(inst.ctx_lens, dtype=torch.int32, device=dev)
+    before = (ctx - T).clamp(min=0).to(torch.int32)
+    n_new = (ctx - before).to(torch.int32)
+
+    def append_all():
+        for ly in inst.layers:
+            PL.append(inst.shape, ly.pool, ly.k_draft, ly.v_draft, n_new, before, inst.table,
+                      ctx_after=ctx)
+
+    us = event_time_us(capture(append_all).replay, reps)
+    per_layer = us / len(inst.layers)
+    return {"tokens_per_seq": T, "layers": len(inst.layers), "us_per_step": us,
+            "us_per_layer": per_layer}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -337,96 +497,18 @@ def main():
         return
 
     from block_sparse_speculative_amd import synth
-    from block_sparse_speculative_amd import workload as WL
-    from block_sparse_speculative_amd.workload import Instance
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w = synth.WORKLOADS[args.workload].with_(draft_tree=args.draft_tree)
-    # Rotate resident copies so one rotation touches more than 2 x 256 MB of
-    # selected data and representatives (the MI355X last-level cache).
-    bytes_per_pass = WL.algorithmic_bytes(w, synth.context_lengths(w, args.seed), w.num_layers)
-    reps_total = args.instances or max(1, -(-2 * 256 * 2 ** 20 // bytes_per_pass))
-    print(f"[bench] workload {w.name}: {bytes_per_pass / 1e6:.1f} MB algorithmic per pass, "
-          f"{reps_total} resident instance(s)", file=sys.stderr, flush=True)
-    def progress(done, total):
-        if done == total or done % 8 == 0:
-            print(f"[bench]   built layer {done}/{total}", file=sys.stderr, flush=True)
-
-    insts = [Instance(w, seed=args.seed + r, num_splits=args.num_splits, with_lse=False,
-                      progress=progress, fused=not args.separate) for r in range(reps_total)]
+    insts, fig = measure(w, args, args.steps, args.warmup, "headline")
     inst0 = insts[0]
-    torch.cuda.synchronize()
-
-    def step():
-        for it in insts:
-            it.step()
-
-    use_graph = not args.no_graph
-    if use_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        run = graph.replay
-    else:
-        run = step
-
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # The graph covers `reps_total` passes; a step is one pass.
-    passes = args.steps * reps_total
-    s_per_pass = wall / passes
-    units = inst0.units()
-    value = units / s_per_pass
-    step_gbs = bytes_per_pass / s_per_pass / 1e9
-
-    # ---- roofline of the attention entry point: a graph of only the attention calls
-    # of every layer (indices from the passes above), replayed between HIP events on
-    # the stream it runs on.
-    attn_graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for it in insts:
-            for l in range(len(it.layers)):
-                it.attend(l)
-    torch.cuda.current_stream().wait_stream(side)
-    with torch.cuda.graph(attn_graph):
-        for it in insts:
-            for l in range(len(it.layers)):
-                it.attend(l)
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    attn_graph.replay()
-    stream.synchronize()
-    reps_attn = max(3, args.steps)
-    ev0.record(stream)
-    for _ in range(reps_attn):
-        attn_graph.replay()
-    ev1.record(stream)
-    ev1.synchronize()
-    launches = reps_attn * reps_total * len(inst0.layers)
-    attn_us = ev0.elapsed_time(ev1) * 1e3 / launches
-    kv_bytes_per_launch = (inst0.selected_tokens() // len(inst0.layers)) * w.head_dim * 2 * (
-        4 if w.dtype == "fp32" else 2)
-    achieved = kv_bytes_per_launch / (attn_us * 1e-6) / 1e9
-
+    s_per_pass = fig["s_per_pass"]
+    step_gbs = fig["bytes_per_pass"] / s_per_pass / 1e9
     result = {
         "metric": METRIC,
-        "value": value,
+        "value": fig["units"] / s_per_pass,
         "unit": "draft-token-heads/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -444,34 +526,60 @@ def main():
             "block_size": w.block_size, "draft_tokens": w.num_draft,
             "draft_structure": w.draft_tree, "k_max": inst0.k_max,
             "reuse": "odd layers reuse" if w.reuse_odd_layers else "none",
-            "splits": inst0.num_splits, "graph": use_graph, "resident_instances": reps_total,
+            "splits": inst0.num_splits, "graph": fig["graph"],
+            "resident_instances": fig["reps_total"],
             "path": ("separate calls: sv_select_blocks / sv_reuse_indices, sv_sparse_verify_attn"
                      if args.separate else
                      "sv_select_and_attend on selecting layers; sv_sparse_verify_attn on the "
                      "previous layer's index buffers on reuse layers"),
         },
         "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
-        "algorithmic_bytes_per_step": bytes_per_pass,
+        "algorithmic_bytes_per_step": fig["bytes_per_pass"],
         "roofline": {
-            "kernel": "sv_sparse_verify_attn (attn_kernel; split merge inside the launch when "
-                      "the grid is resident, else merge_kernel after it)",
+            "kernel": "sv_sparse_verify_attn (attn_kernel; split partials merged inside the "
+                      "launch)",
             "bound": "hbm",
-            "achieved": achieved,
+            "achieved": fig["achieved"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
+            "frac": fig["achieved"] / HBM_PEAK_GBS,
             "traffic": counter_field(w.name, "traffic_bytes_per_launch"),
             "mfma_busy_pct": counter_field(w.name, "mfma_busy_pct"),
-            "avg_launch_us": attn_us,
-            "algorithmic_bytes_per_launch": kv_bytes_per_launch,
+            "avg_launch_us": fig["attn_us"],
+            "algorithmic_bytes_per_launch": fig["kv_bytes_per_launch"],
         },
     }
+    reps = max(3, args.steps)
     if not args.no_dense:
         print("[bench] dense verification at the same context", file=sys.stderr, flush=True)
-        result["dense_vs_sparse"] = dense_vs_sparse(inst0, attn_us, max(3, args.steps))
+        result["dense_vs_sparse"] = dense_vs_sparse(inst0, fig["attn_us"], reps)
+        print("[bench] periodic full verification", file=sys.stderr, flush=True)
+        result["full_verification_schedule"] = full_verification_schedule(
+            inst0, s_per_pass * 1e6, 8, max(3, min(reps, 10)))
     if args.launch_curve:
         print("[bench] attention launch time against selected blocks", file=sys.stderr, flush=True)
-        result["launch_curve"] = launch_curve(inst0, max(3, args.steps))
+        result["launch_curve"] = launch_curve(inst0, reps)
+    print("[bench] decode-step KV append", file=sys.stderr, flush=True)
+    result["decode_append"] = decode_append(inst0, reps)
+    del insts
+    torch.cuda.empty_cache()
+    if not args.no_secondary and args.workload != "qwen128k":
+        # the other graded context length (128K), in the same run
+        wq = synth.WORKLOADS["qwen128k"].with_(draft_tree=args.draft_tree)
+        qi, qf = measure(wq, args, min(args.steps, 10), min(args.warmup, 3), "secondary")
+        result["secondary"] = {
+            "workload": wq.name, "ms_per_step": qf["s_per_pass"] * 1e3,
+            "value": qf["units"] / qf["s_per_pass"], "unit": "draft-token-heads/s",
+            "hbm_frac_step": qf["bytes_per_pass"] / qf["s_per_pass"] / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_step": qf["bytes_per_pass"],
+            "avg_launch_us": qf["attn_us"], "achieved": qf["achieved"],
+            "frac": qf["achieved"] / HBM_PEAK_GBS,
+            "traffic": counter_field(wq.name, "traffic_bytes_per_launch"),
+            "algorithmic_bytes_per_launch": qf["kv_bytes_per_launch"],
+            "resident_instances": qf["reps_total"], "splits": qi[0].num_splits,
+        }
+        del qi
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inst0, args.cpu_seconds)

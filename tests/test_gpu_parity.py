@@ -147,7 +147,7 @@ def test_edge_contexts_empty_partial_forced_only(splits):
     _gpu()
     PT.log(f"[edge] contexts {EDGE.ctx} splits={splits}")
     inst = Instance(EDGE, seed=3, num_splits=splits, nan_pool=True)
-    run_and_check(inst)
+    run_and_check(inst, case=f"edge ctx 0/17/200/1000 s{splits}")
 
 
 def test_single_query_single_head_decode():
@@ -156,7 +156,7 @@ def test_single_query_single_head_decode():
     w = W["llama32k"].with_(num_seqs=2, num_q_heads=4, num_kv_heads=4, num_draft=1,
                             ctx=(3000, 9000), budget=(4096, 64, 50, 1, 1))
     inst = Instance(w, seed=5, nan_pool=True)
-    run_and_check(inst)
+    run_and_check(inst, case="T=1 G=1 decode")
 
 
 @pytest.mark.parametrize("flags", [(0, 0), (1, 0), (0, 1)])
@@ -164,7 +164,7 @@ def test_forced_block_flags(flags):
     _gpu()
     w = W["llama32k"].with_(num_seqs=1, num_q_heads=8, num_kv_heads=2, ctx=(6000,),
                             budget=(0, 5, 0) + flags)
-    run_and_check(Instance(w, seed=9, nan_pool=True))
+    run_and_check(Instance(w, seed=9, nan_pool=True), case=f"forced flags {flags}")
 
 
 def test_k_max_larger_than_budget_pads_with_minus_one():
@@ -172,7 +172,7 @@ def test_k_max_larger_than_budget_pads_with_minus_one():
     w = W["llama32k"].with_(num_seqs=2, num_q_heads=8, num_kv_heads=2, ctx=(5000, 300),
                             budget=(0, 16, 0, 1, 1))
     inst = Instance(w, seed=2, k_max=40, nan_pool=True)
-    run_and_check(inst)
+    run_and_check(inst, case="k_max 40 > budget")
     cnt = inst.layers[0].cnt.cpu()
     assert cnt[0].tolist() == [16, 16] and cnt[1].tolist() == [5, 5]
 
@@ -200,7 +200,7 @@ def test_draft_tree_all_units(name, tree, splits):
     w = TREES[name].with_(draft_tree=tree, num_layers=2, reuse_odd_layers=True)
     a = Instance(w, seed=31, num_splits=splits, nan_pool=True, fused=True)
     assert a.draft_mask is not None
-    run_and_check(a)
+    run_and_check(a, case=f"tree {name} {tree} s{splits}")
     b = Instance(w, seed=31, num_splits=splits, nan_pool=True, fused=False)
     b.step()
     torch.cuda.synchronize()
@@ -234,7 +234,7 @@ def test_full_stack64k_tree_sampled_units():
     PT.log("[full] stack64k random tree")
     w = W["stack64k"].with_(num_layers=2, draft_tree="random")
     inst = Instance(w, seed=33, fused=True)
-    run_and_check(inst, units=[(0, 0), (1, 3), (2, 6), (3, 7)])
+    run_and_check(inst, units=[(0, 0), (1, 3), (2, 6), (3, 7)], case="stack64k random tree")
     del inst
     _free()
 
@@ -250,7 +250,7 @@ def test_full_verification_dense_at_64k_sampled_units():
     w = W["stack64k"].with_(num_layers=2, budget=(1 << 30, 64, 50, 1, 1))
     inst = Instance(w, seed=34, fused=True)
     assert inst.k_max == 1024
-    run_and_check(inst, units=[(0, 0), (3, 7)], check_reps=False)
+    run_and_check(inst, units=[(0, 0), (3, 7)], check_reps=False, case="stack64k dense budget")
     cnt = inst.layers[1].cnt.cpu()
     assert (cnt == 1024).all()
     del inst
@@ -536,7 +536,7 @@ def test_stack_with_reuse_small():
     _gpu()
     w = W["stack64k"].with_(num_seqs=2, num_q_heads=8, num_kv_heads=2, ctx=(8192, 7000))
     inst = Instance(w, seed=13, num_layers=4, nan_pool=True)
-    run_and_check(inst)
+    run_and_check(inst, case="4-layer stack with reuse")
 
 
 # ------------------------------------------------------------------ full sizes
