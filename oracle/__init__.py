@@ -16,3 +16,4 @@ from .sparse_verify import (  # noqa: F401
     merge_partials,
     verify_layer,
 )
+from . import sparse_ffn  # noqa: F401,E402  (the threshold-pruned FFN; see its module)
