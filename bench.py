@@ -482,6 +482,51 @@ def decode_append(inst, reps: int):
             "us_per_layer": per_layer}
 
 
+def sparse_ffn_bench(reps: int, seed: int = 0):
+    """The threshold-pruned FFN of one verification pass (f4): 8 draft tokens through a
+    Llama-3.1-8B-shaped FFN (4096 x 14336), two layers' weights rotated so a replay reads
+    past the 256 MB last-level cache. Algorithmic bytes: all of W_gate plus the W_up and
+    W_down rows of the channels some token keeps. The same call with tau = 0 (every
+    channel kept, the dense FFN) is timed beside it."""
+    import torch
+    from block_sparse_speculative_amd import _lib as L
+    from block_sparse_speculative_amd import synth
+
+    w = synth.FFN_WORKLOADS["ffn_llama8b"]
+    dev = torch.device("cuda")
+    layers = [synth.make_ffn(w, seed + i, dev) for i in range(2)]
+    shape = L.make_ffn_shape(w.num_tokens, w.d_model, w.d_ffn)
+    ws = torch.empty(L.sparse_ffn_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    ys = [torch.empty((w.num_tokens, w.d_model), dtype=torch.bfloat16, device=dev) for _ in layers]
+    keeps = [torch.zeros((w.d_ffn,), dtype=torch.int32, device=dev) for _ in layers]
+
+    def run(tau):
+        def fn():
+            for inp, y, k in zip(layers, ys, keeps):
+                L.sparse_ffn(shape, inp["x"], inp["w_gate"], inp["w_up"], inp["w_down_t"], tau, y,
+                             keep_bits=k, ws=ws)
+        return fn
+
+    sparse_us = event_time_us(capture(run(w.tau)).replay, reps) / len(layers)
+    torch.cuda.synchronize()
+    kept_any = sum(float((k != 0).float().mean()) for k in keeps) / len(keeps)
+    bits = torch.stack(keeps).cpu().to(torch.int64) & 0xFFFFFFFF
+    per_token = float(sum(((bits >> t) & 1).float().mean() for t in range(w.num_tokens))) / w.num_tokens
+    dense_us = event_time_us(capture(run(0.0)).replay, reps) / len(layers)
+    row = w.d_model * 2
+    sparse_bytes = w.d_ffn * row * (1 + 2 * kept_any)
+    dense_bytes = 3 * w.d_ffn * row
+    return {
+        "workload": w.name, "tokens": w.num_tokens, "d_model": w.d_model, "d_ffn": w.d_ffn,
+        "tau": w.tau, "kept_per_token": per_token, "channels_any_token_keeps": kept_any,
+        "sparse_us": sparse_us, "dense_us": dense_us, "speedup": dense_us / sparse_us,
+        "algorithmic_bytes": sparse_bytes,
+        "achieved_gbs": sparse_bytes / (sparse_us * 1e-6) / 1e9,
+        "frac": sparse_bytes / (sparse_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "dense_frac": dense_bytes / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -580,6 +625,9 @@ def main():
         }
         del qi
         torch.cuda.empty_cache()
+    if not args.no_secondary:
+        print("[bench] sparse FFN", file=sys.stderr, flush=True)
+        result["sparse_ffn"] = sparse_ffn_bench(max(3, min(reps, 20)), args.seed)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inst0, args.cpu_seconds)

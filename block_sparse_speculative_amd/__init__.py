@@ -9,5 +9,5 @@ from ._lib import (  # noqa: F401
     attn_num_splits, attn_plan, attn_workspace_bytes, block_repr, budget_blocks, lib,
     make_budget, make_shape, reuse_indices, select_and_attend, select_and_attend_static,
     select_and_attend_workspace_bytes, select_blocks, select_workspace_bytes,
-    sparse_verify_attn,
+    sparse_verify_attn, make_ffn_shape, sparse_ffn, sparse_ffn_workspace_bytes,
 )

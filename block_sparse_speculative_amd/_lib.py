@@ -52,6 +52,11 @@ class AttnPlan(ctypes.Structure):
 MERGE_NONE, MERGE_IN_LAUNCH_WAIT, MERGE_IN_LAUNCH_LAST, MERGE_KERNEL = 0, 1, 2, 3
 
 
+class FfnShape(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("d_ffn", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
 class SvError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{_STATUS.get(status, status)}: {message}")
@@ -84,6 +89,9 @@ _SIG = [
     ("sv_select_and_attend_static", _I, [ctypes.POINTER(Shape), ctypes.POINTER(Budget), _P, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _I, ctypes.c_float, _I, _P,
                                          _P, _P, _P, _P]),
+    ("sv_sparse_ffn_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(FfnShape)]),
+    ("sv_sparse_ffn", _I, [ctypes.POINTER(FfnShape), _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                           ctypes.c_size_t, _P]),
     ("sv_reuse_indices", _I, [ctypes.POINTER(Shape), _I, _P, _P, _P, _P, _P]),
 ]
 EXPORTS = tuple(name for name, _, _ in _SIG)
@@ -325,6 +333,33 @@ def select_and_attend_static(shape: Shape, budget: Budget, q, repr_pool, k_draft
         _ptr(v_draft), _ptr(draft_mask), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
         _ptr(ctx_lens), int(k_max), float(scale), int(num_splits), _ptr(idx), _ptr(cnt),
         _ptr(out), _ptr(lse), _stream()))
+
+
+def make_ffn_shape(num_tokens, d_model, d_ffn, dtype=torch.bfloat16) -> FfnShape:
+    code = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}.get(dtype, dtype)
+    return FfnShape(num_tokens, d_model, d_ffn, code)
+
+
+def sparse_ffn_workspace_bytes(shape: FfnShape) -> int:
+    return lib().sv_sparse_ffn_workspace_bytes(ctypes.byref(shape))
+
+
+def sparse_ffn(shape: FfnShape, x, w_gate, w_up, w_down_t, tau: float, y, keep_bits=None,
+               ws=None):
+    """sv_sparse_ffn: the threshold-pruned gated FFN (x [N, Dm]; w_gate, w_up, w_down_t
+    [F, Dm]; y [N, Dm]; keep_bits [F] int32 viewed as uint32 bits, optional)."""
+    N, Dm, F = shape.num_tokens, shape.d_model, shape.d_ffn
+    _dev(x, "x", torch.bfloat16, (N, Dm))
+    for name, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down_t", w_down_t)):
+        _dev(t, name, torch.bfloat16, (F, Dm))
+    _dev(y, "y", torch.bfloat16, (N, Dm))
+    if keep_bits is not None:
+        _dev(keep_bits, "keep_bits", torch.int32, (F,))
+    if ws is not None:
+        _dev(ws, "ws")
+    _check(lib().sv_sparse_ffn(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(w_up),
+                               _ptr(w_down_t), float(tau), _ptr(y), _ptr(keep_bits), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream()))
 
 
 def reuse_indices(shape: Shape, k_max: int, prev_idx, prev_cnt, idx, cnt):

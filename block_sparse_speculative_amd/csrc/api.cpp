@@ -542,6 +542,84 @@ sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, c
                                     static_cast<hipStream_t>(stream), what);
 }
 
+}  // extern "C"
+
+namespace {
+
+sv_status check_ffn_shape(const sv_ffn_shape* s, const char* what) {
+  if (!s) return fail(SV_ERR_NULL_ARG, "%s: shape is NULL", what);
+  if (s->num_tokens < 0 || s->d_model <= 0 || s->d_ffn <= 0)
+    return fail(SV_ERR_BAD_SHAPE, "%s: sizes must be positive (num_tokens >= 0)", what);
+  if (s->dtype != SV_BF16)
+    return fail(SV_ERR_UNSUPPORTED, "%s: dtype %d not supported (bf16 only)", what, s->dtype);
+  if (s->num_tokens > 16)
+    return fail(SV_ERR_UNSUPPORTED, "%s: num_tokens %d > 16", what, s->num_tokens);
+  if (s->d_model % 512 != 0)
+    return fail(SV_ERR_UNSUPPORTED, "%s: d_model %d not a multiple of 512", what, s->d_model);
+  const int64_t np = sv::ffn_padded_tokens(s->num_tokens);
+  if (np * s->d_model * 2 > 128 * 1024)
+    return fail(SV_ERR_UNSUPPORTED, "%s: %d padded tokens x d_model %d exceed the 128 KB LDS stage",
+                what, static_cast<int>(np), s->d_model);
+  return SV_OK;
+}
+
+struct FfnLayout {
+  size_t mask_off, h_off, part_off, total;
+};
+
+FfnLayout ffn_layout(const sv_ffn_shape* s) {
+  FfnLayout l{};
+  const size_t f = static_cast<size_t>(s->d_ffn);
+  const size_t np = static_cast<size_t>(sv::ffn_padded_tokens(s->num_tokens));
+  l.mask_off = 0;
+  l.h_off = align_up(f * sizeof(uint32_t));
+  l.part_off = l.h_off + align_up(static_cast<size_t>(s->num_tokens) * f * sizeof(float));
+  l.total = l.part_off +
+            align_up(static_cast<size_t>(sv::ffn_chunks(s->d_ffn)) * np * s->d_model * sizeof(float));
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_sparse_ffn_workspace_bytes(const sv_ffn_shape* shape) {
+  if (check_ffn_shape(shape, "sv_sparse_ffn_workspace_bytes") != SV_OK) return 0;
+  return ffn_layout(shape).total;
+}
+
+sv_status sv_sparse_ffn(const sv_ffn_shape* shape, const void* x, const void* w_gate,
+                        const void* w_up, const void* w_down_t, float tau, void* y,
+                        uint32_t* keep_bits, void* ws, size_t ws_bytes, void* stream) {
+  const char* what = "sv_sparse_ffn";
+  if (sv_status st = check_ffn_shape(shape, what)) return st;
+  if (!(tau >= 0.0f) || tau == __builtin_inff())
+    return fail(SV_ERR_BAD_SHAPE, "%s: tau must be finite and >= 0", what);
+  if (shape->num_tokens == 0) return ok();
+  if (!x || !w_gate || !w_up || !w_down_t || !y)
+    return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  const FfnLayout l = ffn_layout(shape);
+  if (!ws || ws_bytes < l.total)
+    return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, l.total,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  char* w = static_cast<char*>(ws);
+  sv::FfnParams p{};
+  p.x = x;
+  p.w_gate = w_gate;
+  p.w_up = w_up;
+  p.w_down_t = w_down_t;
+  p.y = y;
+  p.mask = reinterpret_cast<uint32_t*>(w + l.mask_off);
+  p.h = reinterpret_cast<float*>(w + l.h_off);
+  p.part = reinterpret_cast<float*>(w + l.part_off);
+  p.keep_out = keep_bits;
+  p.tau = tau;
+  p.N = shape->num_tokens;
+  p.Dm = shape->d_model;
+  p.F = shape->d_ffn;
+  return from_hip(sv::launch_ffn(p, static_cast<hipStream_t>(stream)), what);
+}
+
 sv_status sv_reuse_indices(const sv_shape* shape, int32_t k_max, const int32_t* prev_idx,
                            const int32_t* prev_cnt, int32_t* idx, int32_t* cnt, void* stream) {
   const char* what = "sv_reuse_indices";

@@ -74,6 +74,20 @@ struct ReuseParams {
   int64_t n_cnt;
 };
 
+struct FfnParams {
+  const void* x;          // [N, Dm] bf16
+  const void* w_gate;     // [F, Dm] bf16
+  const void* w_up;       // [F, Dm] bf16
+  const void* w_down_t;   // [F, Dm] bf16 (down projection, channel-major)
+  void* y;                // [N, Dm] bf16
+  float* h;               // [N, F] fp32: a * u of kept channels, else 0
+  uint32_t* mask;         // [F] bit t: token t keeps the channel
+  uint32_t* keep_out;     // [F] copy of mask for the caller, or null
+  float* part;            // [chunks, NP, Dm] fp32 partial outputs of the down projection
+  float tau;
+  int32_t N, Dm, F;
+};
+
 // ---------------------------------------------------------------- host launchers
 // Each returns hipSuccess or the launch error; shapes are validated by the caller.
 
@@ -83,6 +97,9 @@ hipError_t launch_score(const SelectParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_topk(const SelectParams& p, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_reuse(const ReuseParams& p, hipStream_t stream);
+hipError_t launch_ffn(const FfnParams& p, hipStream_t stream);
+int ffn_padded_tokens(int n);   // 8 or 16: token rows the FFN kernels are compiled for
+int ffn_chunks(int f);          // channel chunks of the down projection
 
 // How the split partials of a unit are combined.
 enum : int32_t {

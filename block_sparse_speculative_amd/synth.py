@@ -263,3 +263,43 @@ def draft_mask(parents, num_draft: int) -> torch.Tensor:
                 x = par[x]
             m[b, t] = bits
     return m
+
+
+# ---------------------------------------------------------------- sparse FFN inputs
+
+@dataclasses.dataclass(frozen=True)
+class FfnWorkload:
+    """Inputs of the threshold-pruned FFN of one verification pass: the hidden states of
+    the T draft tokens of one sequence (num_tokens rows) entering the FFN of one layer
+    of Llama-3.1-8B's shape (d_model 4096, d_ffn 14336; the tutorial page's evaluated
+    model), and the pruning threshold."""
+    name: str
+    num_tokens: int
+    d_model: int
+    d_ffn: int
+    rho: float      # correlation of the draft tokens' hidden states (one shared component)
+    tau: float      # pruning threshold on |SiLU(gate)|
+
+
+FFN_WORKLOADS = {
+    "ffn_llama8b": FfnWorkload("ffn_llama8b", 8, 4096, 14336, 0.9, 0.30),
+}
+
+
+def make_ffn(w: FfnWorkload, seed: int, device="cpu"):
+    """Draw x [N, Dm] and the weights of one FFN layer, all rounded to bf16.
+
+    x[t] = rho * x_shared + sqrt(1 - rho^2) * z_t with x_shared, z_t ~ N(0, I): the draft
+    tokens of one sequence share most of their hidden state. w_gate and w_up ~
+    N(0, 1/d_model) so a gate pre-activation is ~N(0, 1); w_down_t ~ N(0, 1/d_ffn).
+    Returns dict(x, w_gate, w_up, w_down_t) of torch tensors on `device`."""
+    dev = torch.device(device)
+    g = _gen(seed, 3000, dev)
+    n, dm, f = w.num_tokens, w.d_model, w.d_ffn
+    shared = torch.randn((1, dm), generator=g, device=dev)
+    z = torch.randn((n, dm), generator=g, device=dev)
+    x = (w.rho * shared + math.sqrt(1.0 - w.rho * w.rho) * z).to(torch.bfloat16)
+    wg = (torch.randn((f, dm), generator=g, device=dev) / math.sqrt(dm)).to(torch.bfloat16)
+    wu = (torch.randn((f, dm), generator=g, device=dev) / math.sqrt(dm)).to(torch.bfloat16)
+    wd = (torch.randn((f, dm), generator=g, device=dev) / math.sqrt(f)).to(torch.bfloat16)
+    return dict(x=x, w_gate=wg, w_up=wu, w_down_t=wd)

@@ -294,6 +294,39 @@ sv_status sv_select_and_attend_static(const sv_shape* shape, const sv_budget* bu
                                       int32_t* idx, int32_t* cnt, void* out, float* lse,
                                       void* stream);
 
+/* Sizes of the sparse FFN of a verification pass (the draft tokens' rows). */
+typedef struct sv_ffn_shape {
+  int32_t num_tokens;   /* N: rows (draft tokens) */
+  int32_t d_model;      /* Dm */
+  int32_t d_ffn;        /* F: channels of the FFN */
+  int32_t dtype;        /* sv_dtype; SV_BF16 only */
+} sv_ffn_shape;
+
+/* Bytes of workspace sv_sparse_ffn needs (0 for an invalid shape). */
+size_t sv_sparse_ffn_workspace_bytes(const sv_ffn_shape* shape);
+
+/* Threshold-pruned gated FFN of the verification pass (tutorial page, "Core technique
+ * 2": channels whose intermediate activation is below a threshold tau are pruned at
+ * inference time; sciencestack page, Figure 1 caption: the pruned channels are set by
+ * the output of the activation function and the threshold). With a = SiLU(x W_gate^T):
+ *   token t keeps channel c   iff  |a[t, c]| >= tau
+ *   y[t] = sum over channels c kept by t of  a[t, c] * (x[t] . w_up[c]) * w_down_t[c]
+ * tau = 0 keeps every channel (the dense SwiGLU FFN). Only the w_up and w_down_t rows of
+ * channels some token keeps are read. Accumulation is float32; y is rounded to bf16.
+ *   x         [N, Dm] bf16
+ *   w_gate    [F, Dm] bf16 (row c = channel c's gate weights); w_up likewise
+ *   w_down_t  [F, Dm] bf16 (row c = channel c's output weights: the down projection
+ *             stored channel-major, so a pruned channel's row is skipped whole)
+ *   y         [N, Dm] bf16 out
+ *   keep_bits [F] uint32 out or NULL: bit t of keep_bits[c] = token t keeps channel c
+ *   ws        sv_sparse_ffn_workspace_bytes() bytes (no initialisation needed)
+ * Envelope (else SV_ERR_UNSUPPORTED): bf16; N <= 16; d_model a multiple of 512 with
+ * (N <= 8 ? 8 : 16) * d_model * 2 <= 128 KiB. tau must be finite and >= 0. Three kernels
+ * are enqueued on `stream`. */
+sv_status sv_sparse_ffn(const sv_ffn_shape* shape, const void* x, const void* w_gate,
+                        const void* w_up, const void* w_down_t, float tau, void* y,
+                        uint32_t* keep_bits, void* ws, size_t ws_bytes, void* stream);
+
 /* Inter-layer retrieval reuse (tutorial page, "Core technique 1": some layers take
  * the previous layer's retrieval result instead of selecting again; sciencestack
  * abstract: inter-layer retrieval reuse). Copies prev_idx [B, Hkv, k_max] and
