@@ -16,7 +16,9 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsv.so")
+# The in-tree build; SV_LIBRARY names another build of the same sources instead (the
+# host-sanitizer build, say).
+LIB_PATH = os.environ.get("SV_LIBRARY") or os.path.join(_PKG, "libsv.so")
 
 SV_OK = 0
 SV_F32, SV_BF16 = 0, 1

@@ -51,36 +51,78 @@ def sources():
     return out
 
 
-def _compile(cc, src, obj):
-    cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+# Build with AddressSanitizer and UndefinedBehaviorSanitizer on the host code, for
+# checking the host side of the C ABI (argument validation, workspace layout, error
+# paths) on a machine without a GPU. Every sanitizer flag is given to the host
+# compilation only (-Xarch_host); device code is built as usual, at -O1. The library
+# leaves the sanitizer runtime unresolved; a process that loads it preloads
+# libclang_rt.asan (asan_runtime()).
+SANITIZE_FLAGS = [
+    "-O1",
+    "-g",
+    "-fno-omit-frame-pointer",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (for LD_PRELOAD)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"AddressSanitizer runtime not found ({path!r})")
+    return path
+
+
+def _link(cc, objs, out, extra):
+    out_tmp = out + ".tmp"
+    cmd = [cc, *extra, "-shared", "-fPIC", *objs, "-o", out_tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    return r.stderr
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(out_tmp, out)
 
 
-def build(verbose: bool = False) -> str:
+def _build(out: str, flags, link_flags, verbose: bool) -> str:
     cc = hipcc()
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
     srcs = sources()
     tmp = tempfile.mkdtemp(prefix="sv_build_")
     try:
         objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
         jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+
+        def one(so):
+            src, obj = so
+            cmd = [cc, *flags, "-c", src, "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+            return r.stderr
+
         with cf.ThreadPoolExecutor(jobs) as ex:
-            logs = list(ex.map(lambda so: _compile(cc, *so), zip(srcs, objs)))
+            logs = list(ex.map(one, zip(srcs, objs)))
         if verbose:
             for s, log in zip(srcs, logs):
                 if log.strip():
                     print(f"[{os.path.basename(s)}]\n{log}", file=sys.stderr)
-        out_tmp = LIB + ".tmp"
-        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-        os.replace(out_tmp, LIB)
+        _link(cc, objs, out, link_flags)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    return _build(LIB, HIPCC_FLAGS, [f"--offload-arch={ARCH}"], verbose)
+
+
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """Build the host-only ASan/UBSan library at `out` (see SANITIZE_FLAGS)."""
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"]
+    return _build(out, [*flags, *SANITIZE_FLAGS], [f"--offload-arch={ARCH}"], verbose)
 
 
 if __name__ == "__main__":

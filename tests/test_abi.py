@@ -287,3 +287,43 @@ def test_static_entry_point_rejects_what_its_scratch_cannot_hold():
     assert b"bytes" in lib.sv_last_error()
     assert call(_shape(head_dim=96)) == 3
     assert call(_shape(), k_max=0) == 2
+
+
+def _ffn_shape(n=8, dm=4096, f=14336, dtype=None):
+    s = L.make_ffn_shape(n, dm, f)
+    if dtype is not None:
+        s.dtype = dtype
+    return s
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=17), 3), (dict(n=-1), 2), (dict(dm=0), 2), (dict(f=0), 2), (dict(dm=1000), 3),
+    (dict(n=16, dm=8192), 3),                 # 16 padded tokens x 8192 dims: 256 KB of x
+    (dict(dtype=0), 3),                       # fp32 is not supported
+])
+def test_sparse_ffn_rejects_shapes_before_launch(kw, status):
+    lib = sv.lib()
+    shape = _ffn_shape(**kw)
+    assert lib.sv_sparse_ffn_workspace_bytes(ctypes.byref(shape)) == 0
+    st = lib.sv_sparse_ffn(ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, 0.3, FAKE, None, FAKE,
+                           1 << 40, None)
+    assert st == status
+    assert lib.sv_last_error() != b""
+
+
+def test_sparse_ffn_rejects_tau_null_args_and_workspace():
+    lib = sv.lib()
+    shape = _ffn_shape()
+    need = lib.sv_sparse_ffn_workspace_bytes(ctypes.byref(shape))
+    # mask [F] u32, h [N, F] f32 and the chunk partials [F / 256, 8, Dm] f32, 256-aligned
+    assert need >= 14336 * 4 + 8 * 14336 * 4 + 56 * 8 * 4096 * 4
+    call = lambda tau=0.3, x=FAKE, y=FAKE, ws=FAKE, nbytes=need: lib.sv_sparse_ffn(
+        ctypes.byref(shape), x, FAKE, FAKE, FAKE, tau, y, None, ws, nbytes, None)
+    for tau in (-1.0, float("nan"), float("inf")):
+        assert call(tau=tau) == 2
+    assert call(x=None) == 1 and call(y=None) == 1
+    assert call(ws=None) == 4 and call(nbytes=need - 1) == 4
+    # no tokens: nothing to do, nothing read (null pointers accepted)
+    empty = _ffn_shape(n=0)
+    assert lib.sv_sparse_ffn(ctypes.byref(empty), None, None, None, None, 0.3, None, None,
+                             None, 0, None) == 0
