@@ -85,6 +85,8 @@ def parse():
                     help="skip the qwen128k block that follows the headline workload")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ffn-only", action="store_true",
+                    help="only time the sparse FFN (its JSON record alone, for profiling)")
     return ap.parse_args()
 
 
@@ -482,7 +484,7 @@ def decode_append(inst, reps: int):
             "us_per_layer": per_layer}
 
 
-def sparse_ffn_bench(reps: int, seed: int = 0):
+def sparse_ffn_bench(reps: int, seed: int = 0, graph: bool = True):
     """The threshold-pruned FFN of one verification pass (f4): 8 draft tokens through a
     Llama-3.1-8B-shaped FFN (4096 x 14336), two layers' weights rotated so a replay reads
     past the 256 MB last-level cache. Algorithmic bytes: all of W_gate plus the W_up and
@@ -507,12 +509,15 @@ def sparse_ffn_bench(reps: int, seed: int = 0):
                              keep_bits=k, ws=ws)
         return fn
 
-    sparse_us = event_time_us(capture(run(w.tau)).replay, reps) / len(layers)
+    def timed(fn):
+        return event_time_us(capture(fn).replay if graph else fn, reps) / len(layers)
+
+    sparse_us = timed(run(w.tau))
     torch.cuda.synchronize()
     kept_any = sum(float((k != 0).float().mean()) for k in keeps) / len(keeps)
     bits = torch.stack(keeps).cpu().to(torch.int64) & 0xFFFFFFFF
     per_token = float(sum(((bits >> t) & 1).float().mean() for t in range(w.num_tokens))) / w.num_tokens
-    dense_us = event_time_us(capture(run(0.0)).replay, reps) / len(layers)
+    dense_us = timed(run(0.0))
     row = w.d_model * 2
     sparse_bytes = w.d_ffn * row * (1 + 2 * kept_any)
     dense_bytes = 3 * w.d_ffn * row
@@ -539,6 +544,10 @@ def main():
 
     if args.copy_mib:
         copy_calibration(args.copy_mib, max(1, args.steps))
+        return
+    if args.ffn_only:
+        print(json.dumps(sparse_ffn_bench(max(1, args.steps), args.seed, graph=not args.no_graph)),
+              flush=True)
         return
 
     from block_sparse_speculative_amd import synth
