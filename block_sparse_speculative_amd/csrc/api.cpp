@@ -573,9 +573,9 @@ FfnLayout ffn_layout(const sv_ffn_shape* s) {
   const size_t np = static_cast<size_t>(sv::ffn_padded_tokens(s->num_tokens));
   l.mask_off = 0;
   l.h_off = align_up(f * sizeof(uint32_t));
-  l.part_off = l.h_off + align_up(static_cast<size_t>(s->num_tokens) * f * sizeof(float));
-  l.total = l.part_off +
-            align_up(static_cast<size_t>(sv::ffn_chunks(s->d_ffn)) * np * s->d_model * sizeof(float));
+  l.part_off = l.h_off + align_up(f * 16 * sizeof(float));
+  l.total = l.part_off + align_up(static_cast<size_t>(sv::ffn_ranges(s->d_ffn, s->d_model)) * np *
+                                  s->d_model * sizeof(float));
   return l;
 }
 
@@ -617,6 +617,8 @@ sv_status sv_sparse_ffn(const sv_ffn_shape* shape, const void* x, const void* w_
   p.N = shape->num_tokens;
   p.Dm = shape->d_model;
   p.F = shape->d_ffn;
+  p.dn_range = sv::ffn_range(p.F, p.Dm);
+  p.dn_ranges = sv::ffn_ranges(p.F, p.Dm);
   return from_hip(sv::launch_ffn(p, static_cast<hipStream_t>(stream)), what);
 }
 

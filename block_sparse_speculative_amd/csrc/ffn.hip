@@ -20,12 +20,12 @@
 //    accumulator registers, one instruction per 1 KB of weights), leaving the registers
 //    to loads in flight. The gate totals give a and the keep bits; then only the kept
 //    rows of w_up are read, giving h.
-//  - ffn_down_kernel: channel chunks of 256 x model-dim groups of 512. Each wave gathers
-//    the kept channels of its quarter of the chunk (ballot compaction) and streams those
-//    w_down_t rows, 8 dims per lane, h broadcast from LDS (fp32 FMAs: the rows are
-//    contiguous along the model dimension, not along the summed channels); the four
-//    waves' sums are added in LDS and written as the chunk's partial y.
-//  - ffn_reduce_kernel: y = the chunk partials summed in chunk order (deterministic),
+//  - ffn_down_kernel: one workgroup per (range of channels, 256 model dims). The kept
+//    channels of the range are compacted (ballot) and streamed 32 at a time through an
+//    LDS-DMA ring, W_down rows and their h together; the products are MFMAs whose W^T
+//    operand comes from the gfx950 transposing LDS read and whose h^T operand is h split
+//    into two bf16 parts. Each workgroup writes the partial y of its range.
+//  - ffn_reduce_kernel: y = the range partials summed in range order (deterministic),
 //    rounded to bf16.
 #include "gfx950_mem.h"
 #include "internal.h"
@@ -33,7 +33,6 @@
 namespace sv {
 namespace {
 
-constexpr int kFfnThreads = 256;
 constexpr int kFfnReduceThreads = 64;
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -153,13 +152,12 @@ __global__ __launch_bounds__(kGuThreads) void ffn_gate_up_kernel(FfnParams p) {
   f32x4 u = red[0][lane];
 #pragma unroll
   for (int w = 1; w < kGuWaves; ++w) u += red[w][lane];
-  if (r < p.N) {
-    float* hrow = p.h + static_cast<int64_t>(r) * p.F;
+  // h channel-major, 16 token slots per channel (zero for tokens >= N, whose keep bits
+  // are never set): the down projection streams a channel's 64 bytes with its row.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t c = c0 + 4 * q + e;
-      if (c < p.F) hrow[c] = keep[e] ? a[e] * u[e] : 0.0f;
-    }
+  for (int e = 0; e < 4; ++e) {
+    const int64_t c = c0 + 4 * q + e;
+    if (c < p.F) p.h[c * 16 + r] = keep[e] ? a[e] * u[e] : 0.0f;
   }
   if (lane < 16 && c0 + lane < p.F) {
     p.mask[c0 + lane] = row_bits;
@@ -167,106 +165,180 @@ __global__ __launch_bounds__(kGuThreads) void ffn_gate_up_kernel(FfnParams p) {
   }
 }
 
-constexpr int kFfnChunk = 256;          // channels per down-projection chunk
-constexpr int kFfnDimGroup = 64 * 8;    // model dims per down-projection workgroup
+// ---- down projection (MFMA over W_down tiles read transposed from LDS) ---------------
+//
+// Workgroup (channel range rg, model-dim group dg): the kept channels of its range (a
+// ballot compaction of the keep mask, ascending) are consumed 32 at a time, one MFMA K
+// step each: y^T[256 dims x 16 tokens] += W^T[256 dims x 32 channels] . h^T[32 x 16].
+// W_down_t rows are contiguous along the model dimension, so each tile (32 kept rows x
+// 512 bytes of this dim group, plus the 32 channels' h, 64 bytes each) is staged by
+// LDS-DMA into a 3-deep ring and the A operand is read with the gfx950 transposing LDS
+// read (ds_read_b64_tr_b16: lane (g4, i) receives dim i of 4 consecutive rows; two reads
+// give the 8 channels 8 g4 .. 8 g4 + 7 the MFMA wants per lane). Rows are XOR-swizzled
+// in 32-byte pairs (the swizzle is applied on the global side of the DMA, which keeps
+// every DMA instruction's LDS writes contiguous) so that the 16 rows a read touches fall
+// on distinct banks. h is fp32; the B operand is its split h = hi + lo into two bf16
+// parts (|h - hi - lo| <= 2^-18 |h|), one MFMA each. Each wave owns 64 of the 256 dims,
+// so no cross-wave reduction is needed; the partial of the range is written per token.
+// Pad rows of the last tile re-read the last kept row (already in cache) and take h = 0,
+// so every tile is the same number of DMA instructions and the vmcnt waits are exact.
+constexpr int kDnWaves = 4;
+constexpr int kDnThreads = kDnWaves * 64;
+constexpr int kDnDims = 256;                        // model dims per workgroup
+constexpr int kDnRows = 32;                         // channels per tile (one MFMA K step)
+constexpr int kDnRowBytes = kDnDims * 2;            // 512
+constexpr int kDnWBytes = kDnRows * kDnRowBytes;    // 16 KB of W per tile
+constexpr int kDnHBytes = kDnRows * 64;             // 2 KB of h per tile
+constexpr int kDnTileBytes = kDnWBytes + kDnHBytes;
+constexpr int kDnBuf = 3;                           // ring depth (two tiles in flight)
+constexpr int kDnMaxRange = 512;                    // channels per range at most
+constexpr int kDnWLoads = kDnWBytes / 1024 / kDnWaves;   // W DMA instructions per wave: 4
+static_assert(kDnWLoads == 4 && kDnHBytes == 2048, "tile layout");
+
+// XOR applied to the 16-byte chunk index of row r (0..31): a 3-bit function of the row
+// on the pair index, distinct for the 8 rows each half-wave's transposing read touches.
+__device__ __forceinline__ int dn_swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4_t lds_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(
+          (__attribute__((address_space(3))) char*)(const_cast<char*>(p))));
+}
+
+// bf16 (round to nearest even) bits of a finite float.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
 
 template <int NP>
-__global__ __launch_bounds__(kFfnThreads) void ffn_down_kernel(FfnParams p) {
-  __shared__ float hs[NP][kFfnChunk];
-  __shared__ int list[4][kFfnChunk / 4];
-  __shared__ float red[3][NP][kFfnDimGroup];
+__global__ __launch_bounds__(kDnThreads, 2) void ffn_down_kernel(FfnParams p) {
+  __shared__ __attribute__((aligned(16))) char ring[kDnBuf * kDnTileBytes];
+  __shared__ int list[kDnMaxRange];
+  __shared__ int nk_s;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
   const int Dm = p.Dm;
-  const int64_t cbase = static_cast<int64_t>(blockIdx.x) * kFfnChunk;
-  const int d0 = blockIdx.y * kFfnDimGroup + lane * 8;
-  // h of the chunk (zero past F and for tokens >= N), every load issued before the stores.
-  {
-    constexpr int L = NP * kFfnChunk / kFfnThreads;
-    float v[L];
+  const int rg = blockIdx.x;
+  const int dg = blockIdx.y;
+  const int c0 = rg * p.dn_range;
+  const int cn = p.F - c0 < p.dn_range ? p.F - c0 : p.dn_range;
+
+  // Kept channels of the range, ascending (wave 0; every mask load issued first).
+  if (wave == 0) {
+    constexpr int kSub = kDnMaxRange / 64;
+    bool kk[kSub];
 #pragma unroll
-    for (int k = 0; k < L; ++k) {
-      const int i = tid + k * kFfnThreads;
-      const int t = i / kFfnChunk;
-      const int64_t c = cbase + (i - t * kFfnChunk);
-      v[k] = (t < p.N && c < p.F) ? p.h[static_cast<int64_t>(t) * p.F + c] : 0.0f;
+    for (int s = 0; s < kSub; ++s) {
+      const int c = s * 64 + lane;
+      kk[s] = c < cn && p.mask[c0 + c] != 0u;
     }
+    int nk = 0;
 #pragma unroll
-    for (int k = 0; k < L; ++k) {
-      const int i = tid + k * kFfnThreads;
-      hs[i / kFfnChunk][i % kFfnChunk] = v[k];
-    }
-  }
-  // The kept channels of this wave's quarter of the chunk (ascending), by ballot.
-  int nk = 0;
-  {
-    constexpr int Q = kFfnChunk / 4 / 64;
-    bool kk[Q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int64_t c = cbase + wave * (kFfnChunk / 4) + q * 64 + lane;
-      kk[q] = c < p.F && p.mask[c] != 0u;
-    }
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int j = wave * (kFfnChunk / 4) + q * 64 + lane;
-      const uint64_t b = __builtin_amdgcn_ballot_w64(kk[q]);
-      if (kk[q]) list[wave][nk + __builtin_popcountll(b & ((uint64_t{1} << lane) - 1))] = j;
+    for (int s = 0; s < kSub; ++s) {
+      const uint64_t b = __builtin_amdgcn_ballot_w64(kk[s]);
+      if (kk[s]) list[nk + __builtin_popcountll(b & ((uint64_t{1} << lane) - 1))] = c0 + s * 64 + lane;
       nk += __builtin_popcountll(b);
     }
+    if (lane == 0) nk_s = nk;
   }
   __syncthreads();
-  float acc[NP][8];
+  const int nk = nk_s;
+  const int steps = (nk + kDnRows - 1) / kDnRows;
+
+  f32x4 acc[4];
 #pragma unroll
-  for (int t = 0; t < NP; ++t)
+  for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (steps > 0) {   // workgroup-uniform
+    const uint32_t ring_lds = gmem::lds_address(ring);
+    // Tile s into buffer s % kDnBuf: wave w DMAs W rows 8w .. 8w + 7 (two rows of 512
+    // bytes per instruction) and, waves 0 and 1, the h of channels 16w .. 16w + 15.
+    auto issue = [&](int s) {
+      const uint32_t tb = ring_lds + static_cast<uint32_t>((s % kDnBuf) * kDnTileBytes);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[t][e] = 0.0f;
-  const char* wd = static_cast<const char*>(p.w_down_t);
-  constexpr int U = 16;   // rows in flight per lane
-  for (int i0 = 0; i0 < nk; i0 += U) {
-    uint4 wr[U];
-    int jj[U];
+      for (int j = 0; j < kDnWLoads; ++j) {
+        const int row = 8 * wave + 2 * j + (lane >> 5);
+        const int k = s * kDnRows + row;
+        const int ch = list[k < nk ? k : nk - 1];
+        const int gch = (lane & 31) ^ dn_swz(row);
+        gmem::dma16(p.w_down_t,
+                    (static_cast<uint32_t>(ch) * static_cast<uint32_t>(Dm) + dg * kDnDims + gch * 8) *
+                        2u,
+                    tb + static_cast<uint32_t>((8 * wave + 2 * j) * kDnRowBytes));
+      }
+      if (wave < 2) {
+        const int k = s * kDnRows + 16 * wave + (lane >> 2);
+        const int ch = list[k < nk ? k : nk - 1];
+        gmem::dma16(p.h, static_cast<uint32_t>(ch) * 64u + (lane & 3) * 16u,
+                    tb + kDnWBytes + static_cast<uint32_t>(wave * 1024));
+      }
+    };
+    static_assert(kDnBuf == 3, "the waits below assume at most one younger tile in flight");
+    for (int s = 0; s < kDnBuf - 1 && s < steps; ++s) issue(s);
+    const int md0 = wave * 4;   // this wave's first 16-dim M tile of the group
+    for (int s = 0; s < steps; ++s) {
+      // Tile s landed, with the younger tile already issued (if any) still in flight:
+      // waves 0 and 1 issue kDnWLoads + 1 DMA instructions per tile, the others kDnWLoads.
+      const int younger = steps - 1 - s < kDnBuf - 2 ? steps - 1 - s : kDnBuf - 2;
+      if (younger == 1) {
+        if (wave < 2) gmem::wait_vmcnt<kDnWLoads + 1>();
+        else gmem::wait_vmcnt<kDnWLoads>();
+      } else {
+        gmem::wait_vmcnt<0>();
+      }
+      __syncthreads();   // also: every wave is done with tile s - 1's buffer
+      if (s + kDnBuf - 1 < steps) issue(s + kDnBuf - 1);
+      const char* tb = ring + (s % kDnBuf) * kDnTileBytes;
+      // B operand: channels 8 g4 .. 8 g4 + 7 of the tile, token l16, as hi / lo bf16.
+      uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      jj[u] = i0 + u < nk ? list[wave][i0 + u] : -1;
-      wr[u] = jj[u] >= 0 ? *reinterpret_cast<const uint4*>(wd + ((cbase + jj[u]) * Dm + d0) * 2)
-                         : make_uint4(0u, 0u, 0u, 0u);
-    }
+      for (int jj = 0; jj < 4; ++jj) {
+        uint32_t ph = 0u, pl = 0u;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (jj[u] < 0) continue;
-      const float w[8] = {bf16lo(wr[u].x), bf16hi(wr[u].x), bf16lo(wr[u].y), bf16hi(wr[u].y),
-                          bf16lo(wr[u].z), bf16hi(wr[u].z), bf16lo(wr[u].w), bf16hi(wr[u].w)};
+        for (int e = 0; e < 2; ++e) {
+          const int kk = 8 * g4 + 2 * jj + e;
+          const bool ok = s * kDnRows + kk < nk && l16 < NP;
+          const float h = ok ? *reinterpret_cast<const float*>(tb + kDnWBytes + kk * 64 + l16 * 4)
+                             : 0.0f;
+          const uint32_t bh = bf16_bits(h);
+          const uint32_t bl = bf16_bits(h - __uint_as_float(bh << 16));
+          ph |= bh << (16 * e);
+          pl |= bl << (16 * e);
+        }
+        hi[jj] = ph;
+        lo[jj] = pl;
+      }
+      const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
 #pragma unroll
-      for (int t = 0; t < NP; ++t) {
-        const float hv = hs[t][jj[u]];
+      for (int m = 0; m < 4; ++m) {
+        const int md = md0 + m;
+        s16x4_t half[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[t][e] = __builtin_fmaf(hv, w[e], acc[t][e]);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = 8 * g4 + 4 * hh + (l16 >> 2);
+          const int ch = 2 * md + ((l16 & 3) >> 1);
+          half[hh] = lds_tr16(tb + row * kDnRowBytes + ((ch ^ dn_swz(row)) * 16) + 8 * (l16 & 1));
+        }
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi, acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo, acc[m], 0, 0, 0);
       }
     }
   }
-  // Waves 1..3 hand their sums to wave 0, which writes the chunk's partial.
-  if (wave > 0) {
+  // Partial of the range: lane (g4, l16) holds dims 16 md + 4 g4 .. + 3 of token l16.
+  if (l16 < p.N) {
+    float* dst = p.part + (static_cast<int64_t>(rg) * NP + l16) * Dm + dg * kDnDims;
 #pragma unroll
-    for (int t = 0; t < NP; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[wave - 1][t][lane * 8 + e] = acc[t][e];
-  }
-  __syncthreads();
-  if (wave == 0) {
-    float* part = p.part + (static_cast<int64_t>(blockIdx.x) * NP) * Dm;
-#pragma unroll
-    for (int t = 0; t < NP; ++t) {
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        o[e] = ((acc[t][e] + red[0][t][lane * 8 + e]) + red[1][t][lane * 8 + e]) +
-               red[2][t][lane * 8 + e];
-      float4* dst = reinterpret_cast<float4*>(part + static_cast<int64_t>(t) * Dm + d0);
-      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-    }
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<float4*>(dst + (wave * 4 + m) * 16 + 4 * g4) =
+          make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
   }
 }
 
@@ -277,18 +349,18 @@ __global__ __launch_bounds__(kFfnReduceThreads) void ffn_reduce_kernel(FfnParams
   if (i >= static_cast<int64_t>(p.N) * per_t) return;
   const int t = static_cast<int>(i / per_t);
   const int d = static_cast<int>(i - t * per_t) * 4;
-  const int chunks = (p.F + kFfnChunk - 1) / kFfnChunk;
+  const int ranges = p.dn_ranges;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int B = 8;   // chunk loads in flight
-  for (int k0 = 0; k0 < chunks; k0 += B) {
+  constexpr int B = 8;   // range loads in flight
+  for (int k0 = 0; k0 < ranges; k0 += B) {
     float4 v[B];
 #pragma unroll
     for (int k = 0; k < B; ++k)
-      v[k] = k0 + k < chunks ? *reinterpret_cast<const float4*>(
+      v[k] = k0 + k < ranges ? *reinterpret_cast<const float4*>(
                                    p.part + (static_cast<int64_t>(k0 + k) * NP + t) * p.Dm + d)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < B; ++k) {   // chunk order
+    for (int k = 0; k < B; ++k) {   // range order
       s.x += v[k].x;
       s.y += v[k].y;
       s.z += v[k].z;
@@ -317,8 +389,7 @@ hipError_t launch_np(const FfnParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(ffn_gate_up_kernel<NP>, dim3(gu_blocks), dim3(kGuThreads), lds, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int chunks = (p.F + kFfnChunk - 1) / kFfnChunk;
-  hipLaunchKernelGGL(ffn_down_kernel<NP>, dim3(chunks, p.Dm / kFfnDimGroup), dim3(kFfnThreads), 0,
+  hipLaunchKernelGGL(ffn_down_kernel<NP>, dim3(p.dn_ranges, p.Dm / kDnDims), dim3(kDnThreads), 0,
                      stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -332,7 +403,18 @@ hipError_t launch_np(const FfnParams& p, hipStream_t stream) {
 }  // namespace
 
 int ffn_padded_tokens(int n) { return n <= 8 ? 8 : 16; }
-int ffn_chunks(int f) { return (f + kFfnChunk - 1) / kFfnChunk; }
+// Channels per range of the down projection: about 2 workgroups per CU of a 256-CU GPU
+// over the (range, 256-dim group) grid, a multiple of 64, between 64 and 512.
+int ffn_range(int f, int dm) {
+  const int64_t groups = dm / kDnDims;
+  int64_t r = (static_cast<int64_t>(f) * groups + 511) / 512;
+  r = (r + 63) / 64 * 64;
+  return static_cast<int>(r < 64 ? 64 : r > kDnMaxRange ? kDnMaxRange : r);
+}
+int ffn_ranges(int f, int dm) {
+  const int r = ffn_range(f, dm);
+  return (f + r - 1) / r;
+}
 
 hipError_t launch_ffn(const FfnParams& p, hipStream_t stream) {
   if (p.N == 0) return hipSuccess;

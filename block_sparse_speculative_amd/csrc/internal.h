@@ -80,12 +80,14 @@ struct FfnParams {
   const void* w_up;       // [F, Dm] bf16
   const void* w_down_t;   // [F, Dm] bf16 (down projection, channel-major)
   void* y;                // [N, Dm] bf16
-  float* h;               // [N, F] fp32: a * u of kept channels, else 0
+  float* h;               // [F, 16] fp32: a * u of kept (channel, token), else 0
   uint32_t* mask;         // [F] bit t: token t keeps the channel
   uint32_t* keep_out;     // [F] copy of mask for the caller, or null
-  float* part;            // [chunks, NP, Dm] fp32 partial outputs of the down projection
+  float* part;            // [dn_ranges, NP, Dm] fp32 partial outputs of the down projection
   float tau;
   int32_t N, Dm, F;
+  int32_t dn_range;       // channels per down-projection range (ffn_range)
+  int32_t dn_ranges;      // ranges (ffn_ranges)
 };
 
 // ---------------------------------------------------------------- host launchers
@@ -99,7 +101,8 @@ hipError_t launch_attn(const AttnParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_reuse(const ReuseParams& p, hipStream_t stream);
 hipError_t launch_ffn(const FfnParams& p, hipStream_t stream);
 int ffn_padded_tokens(int n);   // 8 or 16: token rows the FFN kernels are compiled for
-int ffn_chunks(int f);          // channel chunks of the down projection
+int ffn_range(int f, int dm);   // channels per down-projection range
+int ffn_ranges(int f, int dm);  // down-projection ranges
 
 // How the split partials of a unit are combined.
 enum : int32_t {

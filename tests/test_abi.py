@@ -315,8 +315,8 @@ def test_sparse_ffn_rejects_tau_null_args_and_workspace():
     lib = sv.lib()
     shape = _ffn_shape()
     need = lib.sv_sparse_ffn_workspace_bytes(ctypes.byref(shape))
-    # mask [F] u32, h [N, F] f32 and the chunk partials [F / 256, 8, Dm] f32, 256-aligned
-    assert need >= 14336 * 4 + 8 * 14336 * 4 + 56 * 8 * 4096 * 4
+    # mask [F] u32, h [F, 16] f32 and the range partials [32 ranges of 448, 8, Dm] f32
+    assert need >= 14336 * 4 + 14336 * 16 * 4 + 32 * 8 * 4096 * 4
     call = lambda tau=0.3, x=FAKE, y=FAKE, ws=FAKE, nbytes=need: lib.sv_sparse_ffn(
         ctypes.byref(shape), x, FAKE, FAKE, FAKE, tau, y, None, ws, nbytes, None)
     for tau in (-1.0, float("nan"), float("inf")):

@@ -7,11 +7,17 @@ decision is taken in the kernel's precision there); y is then compared with the 
 run on the kernel's decisions. Element bound on y, derived from the arithmetic: the
 output is rounded to bf16 (at most 2^-8 |y|), and every sum is fp32 with at most D
 sequential additions, so each computed dot product is within gamma = D * 2^-24 of its
-sum of absolute terms, with D = (2 Dm/256 + 8) + F/128 + 40. The gate and up products are
-chains of Dm/256 MFMA steps per wave (v_mfma_f32_16x16x32_bf16: 32 products and the
-running sum per step, each step measured on gfx950 to stay within 1.89 * 2^-24 of its own
-sum of absolute terms) followed by the sum of the 8 waves' partials; F/128 + 40 covers
-the per-lane channel loop of the down projection, its wave merge and the chunk sum. Propagated
+sum of absolute terms, with D = (2 Dm/256 + 8) + 256 + 61 + (F/64 + 1) + 8:
+  - the gate and up products are chains of Dm/256 MFMA steps per wave
+    (v_mfma_f32_16x16x32_bf16: 32 products and the running sum per step, each step
+    measured on gfx950 to stay within 1.89 * 2^-24 of its own sum of absolute terms)
+    followed by the sum of the 8 waves' partials;
+  - the down projection takes h as two bf16 parts, h = hi + lo + r with
+    |r| <= 2^-16 |h| (256 units);
+  - it then runs at most 16 MFMA K steps of two MFMAs per channel range (ranges of at
+    most 512 channels: 2 * 1.89 * 16 < 61);
+  - the range partials (at most F/64 + 1 of them) are summed in order;
+  - 8 more cover the rounding of h = a u and slack. Propagated
 through a = SiLU(g) (|SiLU'| <= 1.1), h = a u and y = sum_c h_c w_c:
   |y_gpu - y_ref| <= 2^-8 |y_ref| + gamma * (Y_abs + sum_c |w_cd| (|a_c| U_abs_c
                       + 1.1 |u_c| G_abs_c)) + 4 * 2^-24 * Y_abs,
@@ -59,7 +65,7 @@ def run_ffn(w, seed, tau=None):
     assert (bits >> n == 0).all(), "keep bits set for tokens >= N"
     a = F.gate_activation(x, wg)
     ref_keep = F.kept_channels(a, tau)
-    depth = (2 * dm / 256 + 8) + f / 128 + 40
+    depth = (2 * dm / 256 + 8) + 256 + 61 + (f / 64 + 1) + 8
     gamma = depth * 2.0 ** -24
     g_abs = np.abs(x) @ np.abs(wg).T
     u_abs = np.abs(x) @ np.abs(wu).T
