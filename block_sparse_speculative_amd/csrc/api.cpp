@@ -556,6 +556,9 @@ sv_status check_ffn_shape(const sv_ffn_shape* s, const char* what) {
     return fail(SV_ERR_UNSUPPORTED, "%s: num_tokens %d > 16", what, s->num_tokens);
   if (s->d_model % 512 != 0)
     return fail(SV_ERR_UNSUPPORTED, "%s: d_model %d not a multiple of 512", what, s->d_model);
+  if (static_cast<int64_t>(s->d_ffn) * s->d_model * 2 >= (int64_t{1} << 31))
+    return fail(SV_ERR_UNSUPPORTED, "%s: a %d x %d weight matrix is 2 GiB or more", what,
+                s->d_ffn, s->d_model);
   const int64_t np = sv::ffn_padded_tokens(s->num_tokens);
   if (np * s->d_model * 2 > 128 * 1024)
     return fail(SV_ERR_UNSUPPORTED, "%s: %d padded tokens x d_model %d exceed the 128 KB LDS stage",

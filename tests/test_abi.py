@@ -300,6 +300,7 @@ def _ffn_shape(n=8, dm=4096, f=14336, dtype=None):
     (dict(n=17), 3), (dict(n=-1), 2), (dict(dm=0), 2), (dict(f=0), 2), (dict(dm=1000), 3),
     (dict(n=16, dm=8192), 3),                 # 16 padded tokens x 8192 dims: 256 KB of x
     (dict(dtype=0), 3),                       # fp32 is not supported
+    (dict(dm=8192, f=131072), 3),             # a 2 GiB weight matrix
 ])
 def test_sparse_ffn_rejects_shapes_before_launch(kw, status):
     lib = sv.lib()
