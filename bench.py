@@ -87,6 +87,9 @@ def parse():
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ffn-only", action="store_true",
                     help="only time the sparse FFN (its JSON record alone, for profiling)")
+    ap.add_argument("--append-only", action="store_true",
+                    help="only time the decode-step KV append of the workload (its JSON "
+                         "record alone, for profiling)")
     return ap.parse_args()
 
 
@@ -548,6 +551,14 @@ def main():
     if args.ffn_only:
         print(json.dumps(sparse_ffn_bench(max(1, args.steps), args.seed, graph=not args.no_graph)),
               flush=True)
+        return
+    if args.append_only:
+        from block_sparse_speculative_amd import synth as _synth
+        w = _synth.WORKLOADS[args.workload]
+        inst = build_instances(w, args, 1)[0]
+        rec = decode_append(inst, max(1, args.steps))
+        rec["workload"] = w.name
+        print(json.dumps(rec), flush=True)
         return
 
     from block_sparse_speculative_amd import synth
