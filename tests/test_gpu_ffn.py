@@ -136,3 +136,18 @@ def test_sparse_ffn_bit_identical_run_to_run():
     a = run_ffn(FFN, seed=6)
     b = run_ffn(FFN, seed=6)
     assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["keep"], b["keep"])
+
+
+def test_sparse_ffn_largest_shape_every_element():
+    # Llama-3-70B's FFN shape (d_model 8192, d_ffn 28672; 470 MB per weight matrix):
+    # the widest x stage, the longest gate/up slices and 512-channel down ranges
+    _gpu()
+    w = FFN.__class__("ffn_70b_shape", 8, 8192, 28672, 0.9, 0.3)
+    st = run_ffn(w, seed=9)
+    assert 0.2 < st["kept_any"] < 0.9
+
+
+def test_sparse_ffn_sixteen_tokens_full_size_every_element():
+    # 16 draft tokens (the most the entry point takes) through the Llama-3.1-8B shape
+    _gpu()
+    run_ffn(FFN.__class__("ffn_llama8b_n16", 16, 4096, 14336, 0.9, 0.3), seed=10)
