@@ -35,9 +35,6 @@ namespace {
 
 constexpr int kFfnReduceThreads = 64;
 
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 // ---- gate and up projections (MFMA) ----------------------------------------------------
 //
 // One workgroup = 16 channels (the MFMA's M) x all tokens (N, padded to 16) x the whole
@@ -46,10 +43,11 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 // Operands of v_mfma_f32_16x16x32_bf16 for lane l (r = l % 16, q = l / 16):
 //   A: weight row c0 + r, dims 32 kb + 8 q .. + 7 (one 16-byte load; 16 rows x 64 bytes
 //      per instruction)
-//   B: x of token r at the same dims (from LDS; zero for r >= NP)
+//   B: x of token r at the same dims (from LDS; zero for tokens r >= N)
 //   D: channel c0 + 4 q + e (e = 0..3), token r.
-// x is staged in LDS in fragment order: fragment (kb, q, t) at ((kb * 4 + q) * NP + t) * 16,
-// so the B reads of a wave are consecutive 16-byte pieces (no bank conflicts).
+// x is staged in LDS by LDS-DMA in fragment order: fragment (kb, q, t) at
+// ((kb * 4 + q) * NP + t) * 16, so the B reads of a wave are consecutive 16-byte pieces
+// (no bank conflicts).
 constexpr int kGuWaves = 8;
 constexpr int kGuThreads = kGuWaves * 64;
 constexpr int kGuBatch = 16;   // 16-byte weight loads (MFMA blocks) in flight per lane
