@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "api_internal.h"
@@ -43,6 +44,23 @@ constexpr int kMaxRows = 128;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Alignment the kernels rely on: data arrays, outputs and workspaces are read and
+// written with 16-byte vector accesses and LDS-DMA, int32 and float-scalar arrays with
+// 4-byte ones. NULL (an absent optional buffer) passes.
+struct Buf {
+  const void* p;
+  const char* name;
+  uintptr_t align;
+};
+
+sv_status check_alignment(std::initializer_list<Buf> bufs, const char* what) {
+  for (const Buf& b : bufs)
+    if (b.p && (reinterpret_cast<uintptr_t>(b.p) & (b.align - 1)) != 0)
+      return fail(SV_ERR_UNSUPPORTED, "%s: %s is not %zu-byte aligned", what, b.name,
+                  static_cast<size_t>(b.align));
+  return SV_OK;
+}
 
 // Validates the shape; `what` names the entry point for the message.
 sv_status check_shape(const sv_shape* s, const char* what) {
@@ -287,10 +305,11 @@ sv_status fail_status(sv_status st, const char* fmt, ...) {
 
 sv_status check_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
                                   const float* repr_pool, const void* k_draft,
-                                  const void* v_draft, const void* k_pool, const void* v_pool,
+                                  const void* v_draft, const int32_t* draft_mask,
+                                  const void* k_pool, const void* v_pool,
                                   const int32_t* block_table, const int32_t* ctx_lens,
                                   int32_t k_max, float scale, int32_t num_splits, int32_t* idx,
-                                  int32_t* cnt, void* out, const char* what) {
+                                  int32_t* cnt, void* out, float* lse, const char* what) {
   if (sv_status st = check_shape(shape, what)) return st;
   if (sv_status st = check_budget(budget, what)) return st;
   if (sv_status st = check_kmax(shape, k_max, what)) return st;
@@ -301,7 +320,12 @@ sv_status check_select_and_attend(const sv_shape* shape, const sv_budget* budget
   if (!q || !repr_pool || !k_draft || !v_draft || !k_pool || !v_pool || !block_table ||
       !ctx_lens || !idx || !cnt || !out)
     return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
-  return SV_OK;
+  return check_alignment({{q, "q", 16}, {repr_pool, "repr_pool", 16}, {k_draft, "k_draft", 16},
+                          {v_draft, "v_draft", 16}, {k_pool, "k_pool", 16},
+                          {v_pool, "v_pool", 16}, {out, "out", 16}, {lse, "lse", 4},
+                          {draft_mask, "draft_mask", 4}, {block_table, "block_table", 4},
+                          {ctx_lens, "ctx_lens", 4}, {idx, "idx", 4}, {cnt, "cnt", 4}},
+                         what);
 }
 
 int resolve_splits_checked(const sv_shape* shape, int32_t k_max, int32_t num_splits) {
@@ -396,6 +420,13 @@ sv_status sv_block_repr(const sv_shape* shape, const void* k_new, const void* v_
     if (!k_new || !v_new || !n_new || !ctx_before || !block_table || !k_pool || !v_pool ||
         !repr_pool)
       return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+    if (sv_status st = check_alignment(
+            {{k_new, "k_new", 16}, {v_new, "v_new", 16}, {k_pool, "k_pool", 16},
+             {v_pool, "v_pool", 16}, {repr_pool, "repr_pool", 16}, {n_new, "n_new", 4},
+             {ctx_before, "ctx_before", 4}, {ctx_after, "ctx_after", 4},
+             {block_table, "block_table", 4}},
+            what))
+      return st;
   }
   if (n_new_max > static_cast<int64_t>(shape->max_blocks_per_seq) * shape->block_size)
     return fail(SV_ERR_BAD_SHAPE, "%s: n_new_max exceeds the sequence capacity", what);
@@ -426,6 +457,13 @@ sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const
   if (shape->num_seqs == 0) return ok();
   if (!q || !repr_pool || !block_table || !ctx_lens || !idx || !cnt)
     return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  if (sv_status st = check_alignment({{q, "q", 16}, {repr_pool, "repr_pool", 16},
+                                      {ws, "ws", 16}, {scores, "scores", 4},
+                                      {block_table, "block_table", 4},
+                                      {ctx_lens, "ctx_lens", 4}, {idx, "idx", 4},
+                                      {cnt, "cnt", 4}},
+                                     what))
+    return st;
   size_t scores_off;
   const size_t need = select_ws_layout(shape, &scores_off);
   if (!ws || ws_bytes < need)
@@ -494,6 +532,13 @@ sv_status sv_sparse_verify_attn(const sv_shape* shape, const void* q, const void
   if (!q || !k_draft || !v_draft || !k_pool || !v_pool || !block_table || !ctx_lens || !idx ||
       !cnt || !out)
     return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  if (sv_status st = check_alignment(
+          {{q, "q", 16}, {k_draft, "k_draft", 16}, {v_draft, "v_draft", 16},
+           {k_pool, "k_pool", 16}, {v_pool, "v_pool", 16}, {out, "out", 16}, {ws, "ws", 16},
+           {lse, "lse", 4}, {block_table, "block_table", 4}, {ctx_lens, "ctx_lens", 4},
+           {idx, "idx", 4}, {cnt, "cnt", 4}, {draft_mask, "draft_mask", 4}},
+          what))
+    return st;
   const int splits = resolve_splits(shape, k_max, num_splits);
   const size_t need = attn_ws_bytes(shape, splits);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -526,8 +571,9 @@ sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, c
                                void* stream) {
   const char* what = "sv_select_and_attend";
   if (sv_status st = sv::check_select_and_attend(shape, budget, q, repr_pool, k_draft, v_draft,
-                                                 k_pool, v_pool, block_table, ctx_lens, k_max,
-                                                 scale, num_splits, idx, cnt, out, what))
+                                                 draft_mask, k_pool, v_pool, block_table,
+                                                 ctx_lens, k_max, scale, num_splits, idx, cnt,
+                                                 out, lse, what))
     return st;
   if (shape->num_seqs == 0) return ok();
   const int splits = resolve_splits(shape, k_max, num_splits);
@@ -535,6 +581,7 @@ sv_status sv_select_and_attend(const sv_shape* shape, const sv_budget* budget, c
   if (!ws || ws_bytes < need)
     return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
                 ws ? ws_bytes : static_cast<size_t>(0));
+  if (sv_status st = check_alignment({{ws, "ws", 16}}, what)) return st;
   char* w = static_cast<char*>(ws);
   return sv::select_and_attend_into(shape, budget, q, repr_pool, k_draft, v_draft, draft_mask,
                                     k_pool, v_pool, block_table, ctx_lens, k_max, scale, splits,
@@ -601,6 +648,11 @@ sv_status sv_sparse_ffn(const sv_ffn_shape* shape, const void* x, const void* w_
   if (shape->num_tokens == 0) return ok();
   if (!x || !w_gate || !w_up || !w_down_t || !y)
     return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  if (sv_status st = check_alignment({{x, "x", 16}, {w_gate, "w_gate", 16}, {w_up, "w_up", 16},
+                                      {w_down_t, "w_down_t", 16}, {y, "y", 16}, {ws, "ws", 16},
+                                      {keep_bits, "keep_bits", 4}},
+                                     what))
+    return st;
   const FfnLayout l = ffn_layout(shape);
   if (!ws || ws_bytes < l.total)
     return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, l.total,
@@ -633,6 +685,10 @@ sv_status sv_reuse_indices(const sv_shape* shape, int32_t k_max, const int32_t* 
   if (shape->num_seqs == 0) return ok();
   if (!prev_idx || !prev_cnt || !idx || !cnt)
     return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);
+  if (sv_status st = check_alignment({{prev_idx, "prev_idx", 4}, {prev_cnt, "prev_cnt", 4},
+                                      {idx, "idx", 4}, {cnt, "cnt", 4}},
+                                     what))
+    return st;
   const int64_t units = static_cast<int64_t>(shape->num_seqs) * shape->num_kv_heads;
   const int64_t n_idx = units * k_max;
   auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {

@@ -14,13 +14,15 @@ namespace sv {
 sv_status fail_status(sv_status st, const char* fmt, ...);
 
 // Every host check of sv_select_and_attend except the workspace (shape, budget, k_max,
-// num_splits, scale, pointers). `what` names the entry point in the message.
+// num_splits, scale, pointers and their alignment). `what` names the entry point in the
+// message.
 sv_status check_select_and_attend(const sv_shape* shape, const sv_budget* budget, const void* q,
                                   const float* repr_pool, const void* k_draft,
-                                  const void* v_draft, const void* k_pool, const void* v_pool,
+                                  const void* v_draft, const int32_t* draft_mask,
+                                  const void* k_pool, const void* v_pool,
                                   const int32_t* block_table, const int32_t* ctx_lens,
                                   int32_t k_max, float scale, int32_t num_splits, int32_t* idx,
-                                  int32_t* cnt, void* out, const char* what);
+                                  int32_t* cnt, void* out, float* lse, const char* what);
 
 // Split count the attention uses (sv_attn_num_splits without validation).
 int resolve_splits_checked(const sv_shape* shape, int32_t k_max, int32_t num_splits);

@@ -65,8 +65,9 @@ sv_status sv_select_and_attend_static(const sv_shape* shape, const sv_budget* bu
                                       void* stream) {
   const char* what = "sv_select_and_attend_static";
   if (sv_status st = sv::check_select_and_attend(shape, budget, q, repr_pool, k_draft, v_draft,
-                                                 k_pool, v_pool, block_table, ctx_lens, k_max,
-                                                 scale, num_splits, idx, cnt, out, what))
+                                                 draft_mask, k_pool, v_pool, block_table,
+                                                 ctx_lens, k_max, scale, num_splits, idx, cnt,
+                                                 out, lse, what))
     return st;
   if (shape->num_seqs == 0) return sv::fail_status(SV_OK, "");
   const int64_t units = static_cast<int64_t>(shape->num_seqs) * shape->num_kv_heads;

@@ -25,8 +25,14 @@
  *    indices) are preconditions the host cannot check. Kernels skip entries outside
  *    their valid range instead of reading out of bounds; results for such inputs
  *    are unspecified.
+ *  - Alignment: the kernels read and write data arrays with 16-byte vector
+ *    accesses and direct-to-LDS loads. Every element-typed or float array of a
+ *    head or model dimension (q, drafts, pools, repr_pool, x, weights, out, y) and
+ *    every workspace must be 16-byte aligned; int32 arrays, lse, scores and
+ *    keep_bits 4-byte aligned. A misaligned pointer returns SV_ERR_UNSUPPORTED
+ *    naming it. (hipMalloc and torch allocations are 256-byte aligned.)
  *  - Tensor layouts are dense row-major with the shapes given below.
- *      B   = num_seqs             Hq = num_q_heads      Hkv = num_kv_heads
+ *      B   = num_seqs           Hq = num_q_heads      Hkv = num_kv_heads
  *      G   = Hq / Hkv (GQA group; query head h uses KV head h / G)
  *      D   = head_dim             bs = block_size       T  = num_draft
  *      NB  = max_blocks_per_seq   P  = num_phys_blocks

@@ -328,3 +328,112 @@ def test_sparse_ffn_rejects_tau_null_args_and_workspace():
     empty = _ffn_shape(n=0)
     assert lib.sv_sparse_ffn(ctypes.byref(empty), None, None, None, None, 0.3, None, None,
                              None, 0, None) == 0
+
+
+# Pointer arguments of each entry point, in call order, with the alignment the kernels need
+# (16: vector/LDS-DMA data arrays and workspaces, 4: int32 and scalar-float arrays), and a
+# call builder taking those pointers by name. Every pointer is distinct and 16-byte aligned,
+# so with one of them misaligned, alignment is the only check that can fail before the
+# workspace size (given as large enough). Nothing is launched: every call below fails.
+_A16, _A4 = 16, 4
+
+
+def _ptrs(names):
+    return {n: 0x10000000 * (i + 1) for i, n in enumerate(names)}
+
+
+def _entry_calls():
+    lib = sv.lib()
+    shape = _shape()
+    budget = ctypes.byref(sv.make_budget(4096, 64, 50))
+    fshape = _ffn_shape()
+    P = ctypes.c_void_p
+    big = 1 << 40
+    return {
+        "sv_sparse_verify_attn": (
+            dict(q=_A16, k_draft=_A16, v_draft=_A16, draft_mask=_A4, k_pool=_A16, v_pool=_A16,
+                 block_table=_A4, ctx_lens=_A4, idx=_A4, cnt=_A4, out=_A16, lse=_A4, ws=_A16),
+            lambda a: lib.sv_sparse_verify_attn(
+                ctypes.byref(shape), P(a["q"]), P(a["k_draft"]), P(a["v_draft"]),
+                P(a["draft_mask"]), P(a["k_pool"]), P(a["v_pool"]), P(a["block_table"]),
+                P(a["ctx_lens"]), P(a["idx"]), P(a["cnt"]), 64, 0.1, 0, P(a["out"]), P(a["lse"]),
+                P(a["ws"]), 1 << 30, None)),
+        "sv_select_blocks": (
+            dict(q=_A16, repr_pool=_A16, block_table=_A4, ctx_lens=_A4, idx=_A4, cnt=_A4,
+                 scores=_A4, ws=_A16),
+            lambda a: lib.sv_select_blocks(
+                ctypes.byref(shape), budget, P(a["q"]), P(a["repr_pool"]), P(a["block_table"]),
+                P(a["ctx_lens"]), 64, P(a["idx"]), P(a["cnt"]), P(a["scores"]), P(a["ws"]),
+                1 << 30, None)),
+        "sv_select_and_attend": (
+            dict(q=_A16, repr_pool=_A16, k_draft=_A16, v_draft=_A16, draft_mask=_A4,
+                 k_pool=_A16, v_pool=_A16, block_table=_A4, ctx_lens=_A4, idx=_A4, cnt=_A4,
+                 out=_A16, lse=_A4, ws=_A16),
+            lambda a: lib.sv_select_and_attend(
+                ctypes.byref(shape), budget, P(a["q"]), P(a["repr_pool"]), P(a["k_draft"]),
+                P(a["v_draft"]), P(a["draft_mask"]), P(a["k_pool"]), P(a["v_pool"]),
+                P(a["block_table"]), P(a["ctx_lens"]), 64, 0.1, 0, P(a["idx"]), P(a["cnt"]),
+                P(a["out"]), P(a["lse"]), P(a["ws"]), 1 << 30, None)),
+        "sv_select_and_attend_static": (
+            dict(q=_A16, repr_pool=_A16, k_draft=_A16, v_draft=_A16, draft_mask=_A4,
+                 k_pool=_A16, v_pool=_A16, block_table=_A4, ctx_lens=_A4, idx=_A4, cnt=_A4,
+                 out=_A16, lse=_A4),
+            lambda a: lib.sv_select_and_attend_static(
+                ctypes.byref(shape), budget, P(a["q"]), P(a["repr_pool"]), P(a["k_draft"]),
+                P(a["v_draft"]), P(a["draft_mask"]), P(a["k_pool"]), P(a["v_pool"]),
+                P(a["block_table"]), P(a["ctx_lens"]), 64, 0.1, 0, P(a["idx"]), P(a["cnt"]),
+                P(a["out"]), P(a["lse"]), None)),
+        "sv_block_repr": (
+            dict(k_new=_A16, v_new=_A16, n_new=_A4, ctx_before=_A4, ctx_after=_A4,
+                 block_table=_A4, k_pool=_A16, v_pool=_A16, repr_pool=_A16),
+            lambda a: lib.sv_block_repr(
+                ctypes.byref(shape), P(a["k_new"]), P(a["v_new"]), 8, P(a["n_new"]),
+                P(a["ctx_before"]), P(a["ctx_after"]), P(a["block_table"]), P(a["k_pool"]),
+                P(a["v_pool"]), P(a["repr_pool"]), None)),
+        "sv_reuse_indices": (
+            dict(prev_idx=_A4, prev_cnt=_A4, idx=_A4, cnt=_A4),
+            lambda a: lib.sv_reuse_indices(ctypes.byref(shape), 64, P(a["prev_idx"]),
+                                           P(a["prev_cnt"]), P(a["idx"]), P(a["cnt"]), None)),
+        "sv_sparse_ffn": (
+            dict(x=_A16, w_gate=_A16, w_up=_A16, w_down_t=_A16, y=_A16, keep_bits=_A4, ws=_A16),
+            lambda a: lib.sv_sparse_ffn(
+                ctypes.byref(fshape), P(a["x"]), P(a["w_gate"]), P(a["w_up"]), P(a["w_down_t"]),
+                0.3, P(a["y"]), P(a["keep_bits"]), P(a["ws"]), big, None)),
+    }
+
+
+@pytest.mark.parametrize("entry", ["sv_sparse_verify_attn", "sv_select_blocks",
+                                   "sv_select_and_attend", "sv_select_and_attend_static",
+                                   "sv_block_repr", "sv_reuse_indices", "sv_sparse_ffn"])
+def test_every_misaligned_pointer_is_rejected_by_name(entry):
+    lib = sv.lib()
+    align, call = _entry_calls()[entry]
+    # every pointer in the header's declaration is covered
+    decl = re.search(entry + r"\s*\(([^)]*)\)", re.sub(r"/\*.*?\*/", "", open(HEADER).read(),
+                                                       flags=re.S)).group(1)
+    ptr_args = {m.group(1) for m in re.finditer(r"\*\s*(\w+)", decl)}
+    ptr_args -= {"shape", "budget", "stream"}
+    assert ptr_args == set(align), sorted(ptr_args ^ set(align))
+    for name, need in align.items():
+        for off in sorted({need // 2, need - 4, 2} - {0}):
+            if off % need == 0:
+                continue
+            a = _ptrs(align)
+            a[name] += off
+            assert call(a) == 3, (entry, name, off)
+            msg = lib.sv_last_error().decode()
+            assert f"{name} is not {need}-byte aligned" in msg, msg
+
+
+def test_sixteen_byte_alignment_is_enough():
+    # a pointer 16 bytes past a 256-byte boundary passes the alignment check and the call
+    # goes on to the next one (here: a workspace one byte short), launching nothing
+    lib = sv.lib()
+    shape = _shape()
+    need = sv.select_workspace_bytes(shape, 64)
+    P = ctypes.c_void_p
+    st = lib.sv_select_blocks(ctypes.byref(shape), ctypes.byref(sv.make_budget(4096, 64, 50)),
+                              P(0x10000010), P(0x20000010), P(0x30000004), P(0x40000004), 64,
+                              P(0x50000004), P(0x60000004), P(0x70000004), P(0x80000010),
+                              need - 1, None)
+    assert st == 4 and b"workspace" in lib.sv_last_error()
