@@ -99,19 +99,27 @@ __device__ __forceinline__ void lds_barrier() {
 // One 16-byte LDS-DMA load per lane: lane i's 16 bytes at base + off land at LDS
 // byte address lds + 16*i. base and lds are wave-uniform (the base sits in an SGPR
 // pair), so a lane keeps one 32-bit offset per load rather than a 64-bit pointer.
-// The base is passed through readfirstlane so that it is an SGPR pair even where the
-// register allocator has kept the (uniform) pointer in VGPRs. readfirstlane returns a
-// signed int: each half is converted to uint32_t before it is widened, so a low word
-// with bit 31 set is not sign-extended into the high word.
+// The base and the LDS address are passed through readfirstlane so that they sit in
+// SGPRs even where the register allocator has kept a uniform value in VGPRs.
+// readfirstlane returns a signed int: each half of the base is converted to uint32_t
+// before it is widened, so a low word with bit 31 set is not sign-extended into the high
+// word.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   const uint32_t hi =
       static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
   const uint64_t sa = (static_cast<uint64_t>(hi) << 32) | lo;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
-               "s"(reinterpret_cast<const void*>(sa)), "s"(lds)
-               : "memory", "m0");
+  const uint32_t sl = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
+  // The LDS address goes in through an M0 operand, so the compiler writes M0 itself and
+  // knows this instruction reads it. The compiler cannot see that the asm is a vector
+  // memory instruction, so the asm provides the wait states its operands need: a VMEM
+  // instruction must not read an SGPR within 5 wait states of a VALU write to it (the
+  // base halves come from v_readfirstlane) and an LDS DMA must not read M0 in the wait
+  // state after an SALU write to it. s_nop 4 gives 5 after whatever precedes the asm.
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+               "s"(reinterpret_cast<const void*>(sa)), "{m0}"(sl)
+               : "memory");
 }
 
 // Reductions over the 4 lanes l, l^16, l^32, l^48 (the lanes holding one row) with

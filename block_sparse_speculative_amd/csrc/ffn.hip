@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kGuThreads) void ffn_gate_up_kernel(FfnParams p) {
 // in 32-byte pairs (the swizzle is applied on the global side of the DMA, which keeps
 // every DMA instruction's LDS writes contiguous) so that the 16 rows a read touches fall
 // on distinct banks. h is fp32; the B operand is its split h = hi + lo into two bf16
-// parts (|h - hi - lo| <= 2^-18 |h|), one MFMA each. Each wave owns 64 of the 256 dims,
+// parts (|h - hi - lo| <= 2^-16 |h|), one MFMA each. Each wave owns 64 of the 256 dims,
 // so no cross-wave reduction is needed; the partial of the range is written per token.
 // Pad rows of the last tile re-read the last kept row (already in cache) and take h = 0,
 // so every tile is the same number of DMA instructions and the vmcnt waits are exact.

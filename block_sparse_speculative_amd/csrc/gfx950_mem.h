@@ -40,9 +40,15 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
   const uint64_t sa = (static_cast<uint64_t>(hi) << 32) | lo;
   const uint32_t sl = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
-               "s"(reinterpret_cast<const void*>(sa)), "s"(sl)
-               : "memory", "m0");
+  // The LDS address goes in through an M0 operand, so the compiler writes M0 itself and
+  // knows this instruction reads it. The compiler cannot see that the asm is a vector
+  // memory instruction, so the asm provides the wait states its operands need: a VMEM
+  // instruction must not read an SGPR within 5 wait states of a VALU write to it (the
+  // base halves come from v_readfirstlane) and an LDS DMA must not read M0 in the wait
+  // state after an SALU write to it. s_nop 4 gives 5 after whatever precedes the asm.
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+               "s"(reinterpret_cast<const void*>(sa)), "{m0}"(sl)
+               : "memory");
 }
 
 }  // namespace gmem
