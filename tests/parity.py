@@ -10,6 +10,7 @@ import numpy as np
 import torch
 
 import oracle as O
+from oracle import sparse_ffn as OF
 
 # Output tolerances: fp32 inputs 1e-4 max-abs; bf16 inputs (fp32 accumulation)
 # 1e-2 max-abs and 5e-3 mean-abs. LSE is fp32 arithmetic on exactly representable
@@ -210,3 +211,48 @@ def verify_instance_units(inst, layer: int, units, logical=None, prev_sel=None, 
         sels[(b, g)] = used
     stats["mean_abs"] = mean_sum / max(stats["units"], 1)
     return sels, stats
+
+
+def check_ffn(name, x, wg, wu, wd, tau, bits, yg):
+    """Check one sparse FFN call against the oracle (oracle/sparse_ffn.py): keep decisions
+    exact outside the fp32 band around tau, y within the element bound derived in
+    tests/test_gpu_ffn.py's header. x [N, Dm], the weights [F, Dm] and y [N, Dm] as
+    float64 arrays of the bf16 values; bits [F] the keep bit masks. Returns the observed
+    errors with the keep decisions and y."""
+    n, dm = x.shape
+    f = wg.shape[0]
+    gpu_keep = ((bits[None, :] >> np.arange(n)[:, None]) & 1).astype(bool)
+    assert (bits >> n == 0).all(), "keep bits set for tokens >= N"
+    a = OF.gate_activation(x, wg)
+    ref_keep = OF.kept_channels(a, tau)
+    depth = (2 * dm / 256 + 8) + 256 + 61 + (f / 64 + 1) + 8
+    gamma = depth * 2.0 ** -24
+    g_abs = np.abs(x) @ np.abs(wg).T
+    u_abs = np.abs(x) @ np.abs(wu).T
+    eps = 1.1 * gamma * g_abs + 4 * 2.0 ** -24 * np.abs(a)
+    diff = gpu_keep != ref_keep
+    near = np.abs(np.abs(a) - tau) <= eps
+    assert not (diff & ~near).any(), (
+        f"keep decisions differ outside the fp32 band at {np.argwhere(diff & ~near)[:5].tolist()}")
+    y_ref, _ = OF.sparse_ffn(x, wg, wu, wd, tau, keep=gpu_keep)
+    u = x @ wu.T
+    h = np.where(gpu_keep, a * u, 0.0)
+    y_abs = np.abs(h) @ np.abs(wd)
+    prop = (np.where(gpu_keep, np.abs(a) * u_abs + 1.1 * np.abs(u) * g_abs, 0.0)) @ np.abs(wd)
+    bound = (2.0 ** -8 * np.abs(y_ref) + gamma * (y_abs + prop) + 4 * 2.0 ** -24 * y_abs) * 1.01 \
+        + 1e-30
+    assert np.isfinite(yg).all()
+    err = np.abs(yg - y_ref)
+    frac = err / bound
+    worst = np.unravel_index(int(np.argmax(frac)), frac.shape)
+    assert frac.max() <= 1.0, (f"y error {err[worst]:.3e} above its bound {bound[worst]:.3e} at "
+                               f"{worst} (|y| {abs(y_ref[worst]):.3e})")
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+    kept_any = gpu_keep.any(axis=0).mean()
+    st = dict(units=n, max_abs=float(err.max()), mean_abs=float(err.mean()),
+              rel=float(err.max() / rms) if rms > 0 else 0.0, bound=float(frac.max()),
+              lse=0.0)
+    log(f"  {name} tau={tau}: kept per token {gpu_keep.mean():.3f}, channels any token "
+        f"keeps {kept_any:.3f}, near-threshold mismatches {int(diff.sum())}, {st}")
+    record(f"ffn {name} N{n} Dm{dm} F{f} tau{tau}", **st)
+    return dict(st, kept_any=float(kept_any), keep=gpu_keep, y=yg)

@@ -32,7 +32,6 @@ from block_sparse_speculative_amd import _lib as L
 from block_sparse_speculative_amd import synth
 
 import parity as PT
-from oracle import sparse_ffn as F
 
 pytestmark = pytest.mark.gpu
 
@@ -59,44 +58,8 @@ def run_ffn(w, seed, tau=None):
                  keep_bits=keep_bits, ws=ws)
     torch.cuda.synchronize()
     x, wg, wu, wd = (_np(inp[k]) for k in ("x", "w_gate", "w_up", "w_down_t"))
-    n, dm, f = w.num_tokens, w.d_model, w.d_ffn
     bits = keep_bits.cpu().numpy().astype(np.int64) & 0xFFFFFFFF
-    gpu_keep = ((bits[None, :] >> np.arange(n)[:, None]) & 1).astype(bool)
-    assert (bits >> n == 0).all(), "keep bits set for tokens >= N"
-    a = F.gate_activation(x, wg)
-    ref_keep = F.kept_channels(a, tau)
-    depth = (2 * dm / 256 + 8) + 256 + 61 + (f / 64 + 1) + 8
-    gamma = depth * 2.0 ** -24
-    g_abs = np.abs(x) @ np.abs(wg).T
-    u_abs = np.abs(x) @ np.abs(wu).T
-    eps = 1.1 * gamma * g_abs + 4 * 2.0 ** -24 * np.abs(a)
-    diff = gpu_keep != ref_keep
-    near = np.abs(np.abs(a) - tau) <= eps
-    assert not (diff & ~near).any(), (
-        f"keep decisions differ outside the fp32 band at {np.argwhere(diff & ~near)[:5].tolist()}")
-    y_ref, _ = F.sparse_ffn(x, wg, wu, wd, tau, keep=gpu_keep)
-    u = x @ wu.T
-    h = np.where(gpu_keep, a * u, 0.0)
-    y_abs = np.abs(h) @ np.abs(wd)
-    prop = (np.where(gpu_keep, np.abs(a) * u_abs + 1.1 * np.abs(u) * g_abs, 0.0)) @ np.abs(wd)
-    bound = (2.0 ** -8 * np.abs(y_ref) + gamma * (y_abs + prop) + 4 * 2.0 ** -24 * y_abs) * 1.01 \
-        + 1e-30
-    yg = _np(y)
-    assert np.isfinite(yg).all()
-    err = np.abs(yg - y_ref)
-    frac = err / bound
-    worst = np.unravel_index(int(np.argmax(frac)), frac.shape)
-    assert frac.max() <= 1.0, (f"y error {err[worst]:.3e} above its bound {bound[worst]:.3e} at "
-                               f"{worst} (|y| {abs(y_ref[worst]):.3e})")
-    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
-    kept_any = gpu_keep.any(axis=0).mean()
-    st = dict(units=n, max_abs=float(err.max()), mean_abs=float(err.mean()),
-              rel=float(err.max() / rms) if rms > 0 else 0.0, bound=float(frac.max()),
-              lse=0.0)
-    PT.log(f"  {w.name} tau={tau}: kept per token {gpu_keep.mean():.3f}, channels any token "
-           f"keeps {kept_any:.3f}, near-threshold mismatches {int(diff.sum())}, {st}")
-    PT.record(f"ffn {w.name} N{n} Dm{dm} F{f} tau{tau}", **st)
-    return dict(st, kept_any=float(kept_any), keep=gpu_keep, y=yg)
+    return PT.check_ffn(w.name, x, wg, wu, wd, tau, bits, _np(y))
 
 
 FFN = synth.FFN_WORKLOADS["ffn_llama8b"]
