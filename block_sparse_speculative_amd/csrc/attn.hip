@@ -64,6 +64,7 @@
 // scores, partials and indices are produced and consumed inside one XCD's L2 (a
 // handoff between kernels then costs no memory round trip). This is placement for
 // speed only; kernel boundaries keep the results coherent wherever a workgroup runs.
+#include "gfx950_mem.h"
 #include "internal.h"
 #include "topk_wg.h"
 
@@ -83,43 +84,10 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kBtStageMax = 1024;    // block-table rows up to this length are staged in LDS
 static_assert(kWaveTopkMaxBlocks <= kBtStageMax, "the fused select mode reads the staged row");
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // vmcnt in bits [3:0] and [15:14]; expcnt [6:4] and lgkmcnt [11:8] at maximum.
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Workgroup barrier that orders LDS accesses but leaves the LDS-DMA prefetch in
 // flight.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// One 16-byte LDS-DMA load per lane: lane i's 16 bytes at base + off land at LDS
-// byte address lds + 16*i. base and lds are wave-uniform (the base sits in an SGPR
-// pair), so a lane keeps one 32-bit offset per load rather than a 64-bit pointer.
-// The base and the LDS address are passed through readfirstlane so that they sit in
-// SGPRs even where the register allocator has kept a uniform value in VGPRs.
-// readfirstlane returns a signed int: each half of the base is converted to uint32_t
-// before it is widened, so a low word with bit 31 set is not sign-extended into the high
-// word.
-__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t hi =
-      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
-  const uint64_t sa = (static_cast<uint64_t>(hi) << 32) | lo;
-  const uint32_t sl = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
-  // The LDS address goes in through an M0 operand, so the compiler writes M0 itself and
-  // knows this instruction reads it. The compiler cannot see that the asm is a vector
-  // memory instruction, so the asm provides the wait states its operands need: a VMEM
-  // instruction must not read an SGPR within 5 wait states of a VALU write to it (the
-  // base halves come from v_readfirstlane) and an LDS DMA must not read M0 in the wait
-  // state after an SALU write to it. s_nop 4 gives 5 after whatever precedes the asm.
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
-               "s"(reinterpret_cast<const void*>(sa)), "{m0}"(sl)
-               : "memory");
 }
 
 // Reductions over the 4 lanes l, l^16, l^32, l^48 (the lanes holding one row) with
@@ -310,10 +278,10 @@ __device__ __forceinline__ uint4 lds_read16(const char* base, int chunk) {
 template <class C, int N = C::NBUF - 2>
 __device__ __forceinline__ void wait_for_tile(int n_after) {
   if constexpr (N <= 0) {
-    wait_vmcnt<0>();
+    gmem::wait_vmcnt<0>();
   } else {
     if (n_after >= N) {
-      wait_vmcnt<N * C::LPW>();
+      gmem::wait_vmcnt<N * C::LPW>();
       return;
     }
     wait_for_tile<C, N - 1>(n_after);
@@ -620,7 +588,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
       if (i < p.NB) bt_lds[i] = btv[u];
     }
   }
-  wait_vmcnt<0>();
+  gmem::wait_vmcnt<0>();
   lds_barrier();
 
   // Block descriptors of this split: desc[q] = (physical block, valid tokens of the
@@ -674,7 +642,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
       }
     }
     nsel = nsel_in;
-    wait_vmcnt<0>();   // nothing but the DMA stream is outstanding from here on
+    gmem::wait_vmcnt<0>();   // nothing but the DMA stream is outstanding from here on
     lds_barrier();
   }
   if (nsel > p.k_max) nsel = p.k_max;
@@ -693,8 +661,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
   const char* vdraft = static_cast<const char*>(p.v_draft) +
                        (static_cast<int64_t>(b) * p.T * p.Hkv + g) * D * ES;
   const int64_t draft_row = static_cast<int64_t>(p.Hkv) * D * ES;   // bytes between drafts
-  const uint32_t smem_base =
-      static_cast<uint32_t>((uintptr_t)((__attribute__((address_space(3))) char*)(smem)));
+  const uint32_t smem_base = gmem::lds_address(smem);
 
   // Tile i of this split: the draft tile first (if owned), then context tiles.
   // Context tile -> physical block, token offset inside it, valid tokens (0 for a
@@ -741,7 +708,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
         const int r = q / C::NCHK;
         const int cc = (q % C::NCHK) ^ (is_k ? swz_k<C::NCHK>(r) : swz_v<C>(r));
         const char* base = is_k ? kdraft : vdraft;
-        dma16s(base, static_cast<uint32_t>((r < p.T ? r : 0) * draft_row + cc * 16),
+        gmem::dma16(base, static_cast<uint32_t>((r < p.T ? r : 0) * draft_row + cc * 16),
                lbase + cbase * 16);
       }
     } else {
@@ -753,7 +720,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int u = 0; u < C::LPW; ++u) {
         const int cbase = (u * C::NWAVE + wave) * 64;
-        dma16s(cbase < C::KCH ? kb : vb, dma_off[u], lbase + cbase * 16);
+        gmem::dma16(cbase < C::KCH ? kb : vb, dma_off[u], lbase + cbase * 16);
       }
     }
   };
@@ -956,7 +923,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
   // The last arriver then clears the other arrival word (no workgroup of this launch
   // uses it; every sibling read this launch's epoch before arriving) and advances the
   // epoch, which the next launch on this workspace reads.
-  wait_vmcnt<0>();
+  gmem::wait_vmcnt<0>();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   lds_barrier();
   uint32_t* line = p.tickets + static_cast<int64_t>(unit) * kTicketStride;
