@@ -126,9 +126,21 @@ int resolve_splits(const sv_shape* s, int32_t k_max, int32_t num_splits) {
   if (want <= 0) {
     const int64_t units = static_cast<int64_t>(s->num_seqs) * s->num_kv_heads;
     const int64_t rows = static_cast<int64_t>(s->num_draft) * (s->num_q_heads / s->num_kv_heads);
+    // One workgroup per CU for the builds that take a CU alone (128 rows, fp32). The
+    // others (64 KB ring, two fit a CU) get three workgroups for every two CUs, or two
+    // per CU when each split would still stream 16 tiles or more. A workgroup keeps one
+    // tile in flight, so long streams are bound by each workgroup's latency and gain
+    // from more workgroups, while short ones are bound by the launch's fixed cost, where
+    // more splits only add partials to write and merge.
     const bool one_per_cu = rows > 64 || s->dtype != SV_BF16;
-    const int64_t target_wgs = one_per_cu ? sv::kAttnCUs : sv::kAttnCUs * 3 / 2;
-    want = units > 0 ? target_wgs / units - 1 : 1;
+    if (units <= 0) {
+      want = 1;
+    } else if (one_per_cu) {
+      want = sv::kAttnCUs / units - 1;
+    } else {
+      want = sv::kAttnCUs * 3 / 2 / units - 1;
+      if (want >= 1 && ctx_tiles >= 16 * want) want = sv::kAttnCUs * 2 / units - 1;
+    }
     const int64_t by_tiles = (ctx_tiles + 3) / 4;
     if (want > by_tiles) want = by_tiles;
   }

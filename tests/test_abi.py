@@ -209,11 +209,16 @@ def test_split_ranges_balanced_over_k_max():
 # ------------------------------------------------------------------ launch plans
 
 def test_plan_query_reports_the_launch():
-    # stack64k shape: 4 x 8 units, 11 splits, 64-token tiles, 32 rows, two workgroups per
-    # CU (64 KB ring), the bounded-wait merge in the launch
+    # stack64k shape: 4 x 8 units, 11 splits (short streams of 5-6 tiles: three
+    # workgroups for every two CUs), 64-token tiles, 32 rows, two workgroups per CU
+    # (64 KB ring), the bounded-wait merge in the launch
     p = sv.attn_plan(_shape(num_seqs=4), 64, 0)
     assert p == dict(num_splits=11, workgroups=12 * 32, tile_tokens=64, padded_rows=32,
                      ring_kb=64, merge_mode=L.MERGE_IN_LAUNCH_WAIT)
+    # 128 units (the ragged batch): 2 splits would stream 32 tiles each, so 3 splits
+    # and two workgroups per CU (512)
+    r = sv.attn_plan(_shape(num_seqs=16), 64, 0)
+    assert (r["num_splits"], r["workgroups"], r["ring_kb"]) == (3, 512, 64)
     # qwen128k shape: 2 x 4 units of 128 rows, 128-token tiles, one workgroup per CU
     q = sv.attn_plan(_shape(num_seqs=2, num_kv_heads=4, num_draft=16, block_size=128), 128, 0)
     assert (q["tile_tokens"], q["padded_rows"], q["ring_kb"]) == (128, 128, 128)
