@@ -139,7 +139,13 @@ int resolve_splits(const sv_shape* s, int32_t k_max, int32_t num_splits) {
       want = sv::kAttnCUs / units - 1;
     } else {
       want = sv::kAttnCUs * 3 / 2 / units - 1;
-      if (want >= 1 && ctx_tiles >= 16 * want) want = sv::kAttnCUs * 2 / units - 1;
+      if (want >= 1 && ctx_tiles >= 16 * want) {
+        // not past the split count the launch can still merge in place, if it was within
+        int64_t two = sv::kAttnCUs * 2 / units - 1;
+        if (want < sv::kMaxInKernelParts && two >= sv::kMaxInKernelParts)
+          two = sv::kMaxInKernelParts - 1;
+        want = two;
+      }
     }
     const int64_t by_tiles = (ctx_tiles + 3) / 4;
     if (want > by_tiles) want = by_tiles;

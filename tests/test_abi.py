@@ -219,6 +219,10 @@ def test_plan_query_reports_the_launch():
     # and two workgroups per CU (512)
     r = sv.attn_plan(_shape(num_seqs=16), 64, 0)
     assert (r["num_splits"], r["workgroups"], r["ring_kb"]) == (3, 512, 64)
+    # 12 units with long streams: two per CU would be 41 splits, past the 32 workgroups
+    # per unit the launch merges in place; capped at 31 instead
+    t = sv.attn_plan(_shape(num_seqs=3, num_kv_heads=4, num_q_heads=16), 1024, 0)
+    assert t["num_splits"] == 31 and t["merge_mode"] != L.MERGE_KERNEL
     # qwen128k shape: 2 x 4 units of 128 rows, 128-token tiles, one workgroup per CU
     q = sv.attn_plan(_shape(num_seqs=2, num_kv_heads=4, num_draft=16, block_size=128), 128, 0)
     assert (q["tile_tokens"], q["padded_rows"], q["ring_kb"]) == (128, 128, 128)
