@@ -219,6 +219,10 @@ def test_plan_query_reports_the_launch():
     # and two workgroups per CU (512)
     r = sv.attn_plan(_shape(num_seqs=16), 64, 0)
     assert (r["num_splits"], r["workgroups"], r["ring_kb"]) == (3, 512, 64)
+    # the threshold: 2 splits until each would stream 16 tiles (k_max 32 of 64-token
+    # tiles at block size 64), then 3
+    assert sv.attn_num_splits(_shape(num_seqs=16), 31, 0) == 2
+    assert sv.attn_num_splits(_shape(num_seqs=16), 32, 0) == 3
     # 12 units with long streams: two per CU would be 41 splits, past the 32 workgroups
     # per unit the launch merges in place; capped at 31 instead
     t = sv.attn_plan(_shape(num_seqs=3, num_kv_heads=4, num_q_heads=16), 1024, 0)
