@@ -20,6 +20,7 @@ against the oracle:
 """
 
 import os
+import shutil
 import subprocess
 import sys
 
@@ -39,8 +40,7 @@ def _can_build():
         BC.rocm()
     except RuntimeError:
         return False
-    return os.path.exists(L.LIB_PATH) and bool(
-        __import__("shutil").which("gcc") or __import__("shutil").which("cc"))
+    return os.path.exists(L.LIB_PATH) and bool(shutil.which("gcc") or shutil.which("cc"))
 
 
 def test_c_consumer_compiles_as_c99_and_checks_the_host_abi(tmp_path):
