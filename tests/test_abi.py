@@ -450,3 +450,34 @@ def test_sixteen_byte_alignment_is_enough():
                               P(0x50000004), P(0x60000004), P(0x70000004), P(0x80000010),
                               need - 1, None)
     assert st == 4 and b"workspace" in lib.sv_last_error()
+
+
+def test_last_error_is_per_thread():
+    # the error message is thread-local: threads rejecting different arguments at the
+    # same time each read back the message of their own last call (ctypes drops the
+    # interpreter lock around foreign calls, so the calls overlap)
+    import threading
+    lib = sv.lib()
+    align, call = _entry_calls()["sv_sparse_verify_attn"]
+    names = sorted(align)
+    start = threading.Barrier(16)
+    bad = []
+
+    def worker(t):
+        name = names[t % len(names)]
+        a = _ptrs(align)
+        a[name] += 2
+        start.wait()
+        for _ in range(300):
+            st = call(a)
+            msg = lib.sv_last_error().decode()
+            if st != 3 or f"{name} is not" not in msg:
+                bad.append((t, name, st, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(16)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not bad, bad[:3]
