@@ -114,6 +114,14 @@ sv_status check_kmax(const sv_shape* s, int32_t k_max, const char* what) {
   return SV_OK;
 }
 
+// A selection keeps min(k, k_max) blocks, the forced ones among them, so k_max must
+// hold the forced blocks.
+sv_status check_select_kmax(const sv_budget* b, int32_t k_max, const char* what) {
+  if (k_max < b->keep_first + b->keep_last)
+    return fail(SV_ERR_BAD_SHAPE, "%s: k_max %d smaller than the forced blocks", what, k_max);
+  return SV_OK;
+}
+
 // Split count. Library choice: as many splits as keep every workgroup of the launch
 // resident at once (384 of the 512 slots when two workgroups share a CU, 256 when
 // each needs a CU: 128 padded rows or fp32), but no fewer than about four tiles per
@@ -331,6 +339,7 @@ sv_status check_select_and_attend(const sv_shape* shape, const sv_budget* budget
   if (sv_status st = check_shape(shape, what)) return st;
   if (sv_status st = check_budget(budget, what)) return st;
   if (sv_status st = check_kmax(shape, k_max, what)) return st;
+  if (sv_status st = check_select_kmax(budget, k_max, what)) return st;
   if (num_splits < 0) return fail(SV_ERR_BAD_SHAPE, "%s: num_splits < 0", what);
   if (!(scale > 0.0f) || scale == __builtin_inff())
     return fail(SV_ERR_BAD_SHAPE, "%s: scale must be finite and positive", what);
@@ -472,6 +481,7 @@ sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const
   if (sv_status st = check_shape(shape, what)) return st;
   if (sv_status st = check_budget(budget, what)) return st;
   if (sv_status st = check_kmax(shape, k_max, what)) return st;
+  if (sv_status st = check_select_kmax(budget, k_max, what)) return st;
   if (shape->num_seqs == 0) return ok();
   if (!q || !repr_pool || !block_table || !ctx_lens || !idx || !cnt)
     return fail(SV_ERR_NULL_ARG, "%s: a required pointer is NULL", what);

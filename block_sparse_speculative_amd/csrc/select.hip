@@ -10,8 +10,8 @@
 //                blocks [Cc, Cc+C) of sequence b for KV head g, streaming the
 //                float32 representatives through the block table (one 16-byte load
 //                per lane, D/4 lanes per block, DPP reduction in a fixed order).
-//                Sequences whose budget keeps every block are skipped unless the
-//                caller asked for the scores.
+//                Sequences that keep every block (budget capped at k_max >= nb)
+//                are skipped unless the caller asked for the scores.
 //  top-k         grid = (Hkv, B): budget, then
 //                 - NB <= 1024: the keys spread over the registers of four
 //                   wavefronts, LDS radix select with a single-register finish and
@@ -105,8 +105,11 @@ __global__ __launch_bounds__(NT) void score_kernel(SelectParams p) {
   const int sub = lane / LPB;
   const int li = lane % LPB;
   const int j0 = chunk * CHUNK;
-  // A sequence whose budget keeps every block needs no scores.
-  const bool dense = budget_of(p, ctx, nb) >= nb;
+  // A sequence that keeps every block needs no scores: its budget, capped at k_max
+  // as the top-k caps it, reaches nb.
+  int kcap = budget_of(p, ctx, nb);
+  if (kcap > p.k_max) kcap = p.k_max;
+  const bool dense = kcap >= nb;
   if (j0 < nb && (!dense || p.scores_requested)) {
     const E* q = static_cast<const E*>(p.q) + static_cast<int64_t>(b) * p.T * p.Hq * D;
     // Block-table loads first, then the query loads, then all representative loads

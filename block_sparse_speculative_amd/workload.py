@@ -40,7 +40,7 @@ class Instance:
                  ctx_lens: Optional[List[int]] = None, paged: Optional[bool] = None,
                  num_splits: int = 0, with_lse: bool = True, nan_pool: bool = False,
                  k_max: Optional[int] = None, append_chunk: int = 0, progress=None,
-                 fused: bool = False, layer_offset: int = 0):
+                 fused: bool = False, layer_offset: int = 0, cap_selection: bool = False):
         if paged is not None:
             w = w.with_(paged=paged)
         self.w = w
@@ -58,7 +58,9 @@ class Instance:
                                   w.block_size, table.shape[1], P, w.num_draft, w.torch_dtype)
         self.budget = L.make_budget(*w.budget)
         need = max([L.budget_blocks(self.budget, c, w.block_size) for c in self.ctx_lens] + [1])
-        self.k_max = max(need, k_max or 0)
+        # k_max is at least every sequence's budget, unless cap_selection asks for the
+        # given k_max as it is (below a budget it caps the selection)
+        self.k_max = k_max if (cap_selection and k_max) else max(need, k_max or 0)
         self.scale = synth.softmax_scale(w)
         self.ws = PL.Workspaces(self.shape, self.k_max, num_splits, self.device)
         self.num_splits = L.attn_num_splits(self.shape, self.k_max, num_splits)

@@ -148,17 +148,20 @@ size_t sv_select_workspace_bytes(const sv_shape* shape, int32_t k_max);
  *
  * For sequence b and KV head g, with nb = ceil(ctx_lens[b]/bs):
  *   score[j] = sum over the G query heads h of g of  q[b,0,h,:] . repr_pool[bt[b,j], g, :]
- * computed in float32 (unscaled). k = budget(ctx_lens[b]). If k >= nb every block
- * is selected; otherwise the forced blocks plus the k - |forced| best other blocks
- * by score (ties to the lower index; NaN ranks lowest).
+ * computed in float32 (unscaled). k = min(budget(ctx_lens[b]), k_max). If k >= nb
+ * every block is selected; otherwise the forced blocks plus the k - |forced| best
+ * other blocks by score (ties to the lower index; NaN ranks lowest).
  *   q          [B, T, Hq, D] dtype; only draft token 0 is read
  *   idx        [B, Hkv, k_max] int32 out: ascending logical indices, padded with -1
- *   cnt        [B, Hkv]        int32 out: number of selected blocks (= min(k, k_max))
+ *   cnt        [B, Hkv]        int32 out: number of selected blocks (= min(k, nb))
  *   scores     [B, Hkv, NB]    float32 out, optional (NULL): the block scores
- * k_max must be >= k for every sequence (use sv_budget_blocks); otherwise only
- * the first k_max selected blocks (in ascending order) are kept. `ws` must hold sv_select_workspace_bytes() bytes (scratch for
- * the scores when `scores` is NULL); its contents need no initialisation. Two
- * kernels are enqueued (scoring, then budget + top-k). */
+ * With k_max >= budget(ctx_lens[b]) for every sequence (sv_budget_blocks gives it)
+ * the selection is the method's; a smaller k_max caps the budget as above (a
+ * sequence whose budget keeps every block then also gets the best k_max by score).
+ * k_max < keep_first + keep_last is rejected (SV_ERR_BAD_SHAPE). `ws` must hold
+ * sv_select_workspace_bytes() bytes (scratch for the scores when `scores` is NULL);
+ * its contents need no initialisation. Two kernels are enqueued (scoring, then
+ * budget + top-k). */
 sv_status sv_select_blocks(const sv_shape* shape, const sv_budget* budget, const void* q,
                            const float* repr_pool, const int32_t* block_table,
                            const int32_t* ctx_lens, int32_t k_max, int32_t* idx,

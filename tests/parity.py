@@ -70,12 +70,15 @@ def unit_inputs(logical, b: int, g: int, group: int) -> UnitInputs:
         ctx=ctx)
 
 
-def oracle_select(u: UnitInputs, bs: int, budget, group: int):
-    """Oracle scores and selection of one (sequence, KV head) unit."""
+def oracle_select(u: UnitInputs, bs: int, budget, group: int, k_max=None):
+    """Oracle scores and selection of one (sequence, KV head) unit. A `k_max` below the
+    budget caps it (the C ABI's documented cap: the oracle selects with min(k, k_max))."""
     dense, mn, frac, kf, kl = budget
     reps = O.block_representatives(u.k_ctx, bs)
     scores = O.block_scores(u.q[0], reps, group)[0]
     k = O.budget_blocks(u.ctx, bs, dense, mn, frac)
+    if k_max is not None:
+        k = min(k, k_max)
     sel = O.select_blocks(scores, k, bool(kf), bool(kl))
     return reps[:, 0], scores, k, sel
 
@@ -186,7 +189,7 @@ def verify_instance_units(inst, layer: int, units, logical=None, prev_sel=None, 
             assert gsel == [int(x) for x in prev_sel[(b, g)]], "reuse layer changed the selection"
             used = np.array(gsel, dtype=np.int64)
         else:
-            reps, scores, k, osel = oracle_select(u, bs, w.budget, G)
+            reps, scores, k, osel = oracle_select(u, bs, w.budget, G, inst.k_max)
             assert int(cnt[b, g]) == min(k, nb)
             kind = check_selection(gsel, osel, scores, k, nb, kf, kl)
             stats[kind] += 1

@@ -147,6 +147,10 @@ def test_select_rejects_bad_budget_and_workspace():
     assert call(good, ws_bytes=need - 1) == 4
     assert call(good, q=None) == 1
     assert call(good, k_max=0) == 2
+    # k_max caps the budget but must hold the forced blocks
+    assert call(good, k_max=1) == 2 and b"forced" in lib.sv_last_error()
+    assert call(ctypes.byref(sv.make_budget(4096, 64, 50, 1, 0)), k_max=1, ws_bytes=0) == 4
+    assert call(ctypes.byref(sv.make_budget(4096, 64, 50, 0, 0)), k_max=1, ws_bytes=0) == 4
 
 
 def test_repr_and_reuse_reject_before_launch():
@@ -191,6 +195,9 @@ def test_select_and_attend_rejects_before_launch():
     assert call(ws_bytes=need - 1) == 4
     assert call(q=None) == 1
     assert call(k_max=0) == 2
+    assert call(k_max=1) == 2 and b"forced" in lib.sv_last_error()
+    assert call(budget=ctypes.byref(sv.make_budget(4096, 64, 50, 1, 0)), k_max=1,
+                ws_bytes=0) == 4
     assert call(scale=0.0) == 2
     assert call(splits=-1) == 2
     assert lib.sv_select_and_attend(ctypes.byref(_shape(head_dim=96)), good, FAKE, FAKE, FAKE,

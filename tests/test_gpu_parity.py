@@ -177,6 +177,41 @@ def test_k_max_larger_than_budget_pads_with_minus_one():
     assert cnt[0].tolist() == [16, 16] and cnt[1].tolist() == [5, 5]
 
 
+# k_max below the budget caps it: min(k, k_max) blocks, the forced ones and the best
+# others by score, also for sequences whose budget keeps every block (their scores
+# must then be computed). The oracle selects with the capped budget.
+CAPS = {
+    "sparse_budget": (SMALL["llama_small"], 20),
+    "dense_budget": (SMALL["llama_small"].with_(budget=(16384, 64, 50, 1, 1)), 40),
+    "forced_only": (SMALL["llama_small"], 2),
+    "first_only": (SMALL["llama_small"].with_(budget=(0, 8, 0, 1, 0)), 1),
+    "ragged_mixed": (SMALL["ragged_small"], 50),            # one dense, two sparse budgets
+    "long_table": (SMALL["long_table"], 30),                # > 1024 blocks: LDS radix top-k
+    "long_table_dense_budget": (SMALL["long_table"].with_(budget=(65536, 64, 50, 1, 1)), 200),
+}
+
+
+@pytest.mark.parametrize("name", list(CAPS))
+def test_k_max_below_the_budget_caps_the_selection(name):
+    _gpu()
+    w, k_max = CAPS[name]
+    PT.log(f"[cap] {name} k_max={k_max}")
+    runs = []
+    for fused in (False, True):
+        inst = Instance(w, seed=23, k_max=k_max, cap_selection=True, nan_pool=True,
+                        fused=fused)
+        assert inst.k_max == k_max
+        run_and_check(inst, case=f"cap {name} {'fused' if fused else 'separate'}")
+        assert int(inst.layers[0].cnt.max()) <= k_max
+        runs.append(inst)
+    a, b = runs
+    for la, lb in zip(a.layers, b.layers):
+        assert torch.equal(la.idx, lb.idx) and torch.equal(la.cnt, lb.cnt)
+        assert torch.equal(la.out, lb.out) and torch.equal(la.lse, lb.lse)
+    del a, b, runs
+    _free()
+
+
 # ------------------------------------------------------------------ draft trees
 
 TREES = {
