@@ -340,7 +340,8 @@ sv_status sv_sparse_ffn(const sv_ffn_shape* shape, const void* x, const void* w_
 /* Inter-layer retrieval reuse (tutorial page, "Core technique 1": some layers take
  * the previous layer's retrieval result instead of selecting again; sciencestack
  * abstract: inter-layer retrieval reuse). Copies prev_idx [B, Hkv, k_max] and
- * prev_cnt [B, Hkv] into idx / cnt. The buffers must not overlap. */
+ * prev_cnt [B, Hkv] into idx / cnt. Source and destination must not overlap
+ * (SV_ERR_BAD_SHAPE otherwise). */
 sv_status sv_reuse_indices(const sv_shape* shape, int32_t k_max, const int32_t* prev_idx,
                            const int32_t* prev_cnt, int32_t* idx, int32_t* cnt, void* stream);
 
