@@ -114,3 +114,48 @@ def test_sparse_ffn_sixteen_tokens_full_size_every_element():
     # 16 draft tokens (the most the entry point takes) through the Llama-3.1-8B shape
     _gpu()
     run_ffn(FFN.__class__("ffn_llama8b_n16", 16, 4096, 14336, 0.9, 0.3), seed=10)
+
+
+# ---- seeded sweep over the envelope: token counts 1-16, model dims 512 x 1..8 (within
+# the x-staging limit), channel counts at and around the 16-channel gate tiles and the
+# 64-channel range granule as well as ragged ones, thresholds from dense to prune-all,
+# and token correlations from none to strong.
+NUM_FFN_CASES = 24
+
+
+def ffn_sweep_case(i: int):
+    r = np.random.default_rng(104729 * i + 3)
+    n = int(r.integers(1, 17))
+    dm_max = 8 if n <= 8 else 4
+    dm = 512 * int(r.integers(1, dm_max + 1))
+    if r.random() < 0.4:
+        f = int(r.choice([1, 15, 16, 17, 63, 64, 65, 511, 512, 513]))
+    else:
+        f = int(r.integers(100, 6001))
+    u = r.random()
+    tau = 0.0 if u < 0.15 else (8.0 if u < 0.25 else float(r.uniform(0.05, 0.8)))
+    rho = float(r.choice([0.0, 0.5, 0.9]))
+    return FFN.__class__(f"sweep{i}_n{n}_dm{dm}_f{f}", n, dm, f, rho, tau)
+
+
+def test_ffn_sweep_inside_the_envelope():
+    names = set()
+    for i in range(NUM_FFN_CASES):
+        w = ffn_sweep_case(i)
+        assert 1 <= w.num_tokens <= 16 and w.d_model % 512 == 0
+        assert (8 if w.num_tokens <= 8 else 16) * w.d_model * 2 <= 128 * 1024
+        names.add(w.name)
+    assert len(names) == NUM_FFN_CASES
+
+
+@pytest.mark.parametrize("i", range(NUM_FFN_CASES))
+def test_sparse_ffn_sweep_every_element(i):
+    _gpu()
+    w = ffn_sweep_case(i)
+    PT.log(f"[ffn sweep {i}] N {w.num_tokens} Dm {w.d_model} F {w.d_ffn} tau {w.tau:.3f} "
+           f"rho {w.rho}")
+    st = run_ffn(w, seed=200 + i)
+    if w.tau == 0.0:
+        assert st["keep"].all()
+    if w.tau >= 8.0:
+        assert not st["keep"].any() and (st["y"] == 0.0).all()
