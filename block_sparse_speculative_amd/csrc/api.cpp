@@ -122,10 +122,10 @@ sv_status check_select_kmax(const sv_budget* b, int32_t k_max, const char* what)
   return SV_OK;
 }
 
-// Split count. Library choice: as many splits as keep every workgroup of the launch
-// resident at once (384 of the 512 slots when two workgroups share a CU, 256 when
-// each needs a CU: 128 padded rows or fp32), but no fewer than about four tiles per
-// split, so the per-workgroup prologue and the merge stay small next to the stream.
+// Split count. Library choice: a grid that is resident at once (256 workgroups when
+// each needs a CU: 128 padded rows or fp32; else 384 of the 512 slots of two per CU,
+// or all 512 for long streams), but no more splits than about one per four tiles, so
+// the per-workgroup prologue and the merge stay small next to the stream.
 int resolve_splits(const sv_shape* s, int32_t k_max, int32_t num_splits) {
   const int tt = sv::attn_tile_tokens(s->block_size, s->dtype == SV_BF16,
                                      s->num_draft * (s->num_q_heads / s->num_kv_heads));
@@ -148,7 +148,7 @@ int resolve_splits(const sv_shape* s, int32_t k_max, int32_t num_splits) {
     } else {
       want = sv::kAttnCUs * 3 / 2 / units - 1;
       if (want >= 1 && ctx_tiles >= 16 * want) {
-        // not past the split count the launch can still merge in place, if it was within
+        // keep a count that merged inside the launch (at most 31 context splits) there
         int64_t two = sv::kAttnCUs * 2 / units - 1;
         if (want < sv::kMaxInKernelParts && two >= sv::kMaxInKernelParts)
           two = sv::kMaxInKernelParts - 1;
