@@ -332,7 +332,8 @@ size_t sv_sparse_ffn_workspace_bytes(const sv_ffn_shape* shape);
  * Envelope (else SV_ERR_UNSUPPORTED): bf16; N <= 16; d_model a multiple of 512 with
  * (N <= 8 ? 8 : 16) * d_model * 2 <= 128 KiB; each weight matrix under 2 GiB
  * (d_ffn * d_model * 2 < 2^31: the kernels address rows with 32-bit byte offsets). tau
- * must be finite and >= 0. Three kernels are enqueued on `stream`. */
+ * must be finite and >= 0. Three kernels are enqueued on `stream`; with num_tokens = 0
+ * nothing is enqueued and keep_bits is left as it was. */
 sv_status sv_sparse_ffn(const sv_ffn_shape* shape, const void* x, const void* w_gate,
                         const void* w_up, const void* w_down_t, float tau, void* y,
                         uint32_t* keep_bits, void* ws, size_t ws_bytes, void* stream);
