@@ -24,7 +24,7 @@ from oracle import sparse_verify as O
 import parity as PT
 from test_gpu_parity import run_and_check
 
-NUM_CASES = 64
+NUM_CASES = 256
 
 
 def sweep_case(i: int):
