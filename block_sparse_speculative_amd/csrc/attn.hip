@@ -214,7 +214,11 @@ struct Cfg {
   // has it alone); vmcnt holds at most 63 outstanding loads.
   static constexpr int RING_KB = RING_KB_;
   // Workgroups per CU: two with a 64 KB ring (bf16; fp32 needs the registers of one).
-  static constexpr int MINB = (RING_KB <= 64 && BF16) ? 2 : 1;
+  // The second __launch_bounds__ argument is the minimum number of waves per SIMD (EU):
+  // two workgroups of NWAVE waves on the CU's four SIMDs need ceil(2 * NWAVE / 4); a
+  // workgroup that has the CU alone asks for no more than one.
+  static constexpr int WG_PER_CU = (RING_KB <= 64 && BF16) ? 2 : 1;
+  static constexpr int MIN_WAVES_PER_EU = WG_PER_CU == 2 ? (2 * NWAVE + 3) / 4 : 1;
   static constexpr int NBUF_VM = 1 + 63 / LPW;
   static constexpr int NBUF_LDS = RING_KB * 1024 / TILE_BYTES;
   static constexpr int NBUF_CAP = 8;
@@ -464,7 +468,7 @@ __device__ __forceinline__ void attend_group(WaveState<C>& st, const char* kbase
 }
 
 template <class C, bool TOPK>
-__global__ __launch_bounds__(C::NT, C::MINB) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(C::NT, C::MIN_WAVES_PER_EU) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   constexpr int ES = C::ES;
   constexpr int D = C::D;
@@ -1069,7 +1073,7 @@ hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
     case 16: return launch_ring<BF16, D, TT, 16>(p, stream);
     case 32: return launch_ring<BF16, D, TT, 32>(p, stream);
     case 64: return launch_ring<BF16, D, TT, 64>(p, stream);
-    default: return launch_ring<BF16, D, TT, 128>(p, stream);
+    default: return launch_cfg<Cfg<BF16, D, TT, 128, 128>>(p, stream);   // always one per CU
   }
 }
 
