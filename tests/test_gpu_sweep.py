@@ -48,6 +48,11 @@ def sweep_case(i: int):
             c = int(r.integers(bs, 9000))               # ragged
         ctx.append(c)
     ctx[0] = max(ctx[0], 3 * bs)
+    if i % 16 == 5:
+        # every 16th draw from 5 on: a row of more than 1024 blocks (the separate top-k
+        # kernel, also behind the fused call)
+        bs = 32
+        ctx[0] = int(np.random.default_rng(1_000_003 + i).integers(33_000, 45_000))
     kf, kl = int(r.integers(0, 2)), int(r.integers(0, 2))
     forced = kf + kl
     budget = (int(r.choice([0, 2048, 6000])), int(r.integers(max(forced, 1), 25)),
@@ -62,6 +67,8 @@ def sweep_case(i: int):
     else:
         k_max, cap = int(r.integers(max(forced, 1), max(need, max(forced, 1)) + 1)), True
     splits = int(r.choice([0, 0, 1, 2, 3, 7, 20]))
+    if i % 16 == 9:
+        splits = 40   # every 16th draw from 9 on: the merge kernel when k_max allows it
     fused = bool(r.integers(0, 2))
     tree = str(r.choice(["chain", "random", "star"]))
     paged = bool(r.integers(0, 2))
