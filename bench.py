@@ -419,7 +419,9 @@ def measure(w, args, steps: int, warmup: int, label: str):
     elem = 4 if w.dtype == "fp32" else 2
     kv_bytes_per_launch = (inst0.selected_tokens() // len(inst0.layers)) * w.head_dim * 2 * elem
     achieved = kv_bytes_per_launch / (attn_us * 1e-6) / 1e9
+    all_bytes = WL.all_bytes(w, inst0.ctx_lens, len(inst0.layers), inst0.k_max, inst0.num_splits)
     fig = dict(s_per_pass=s_per_pass, units=inst0.units(), bytes_per_pass=bytes_per_pass,
+               all_bytes_per_pass=all_bytes,
                attn_us=attn_us, kv_bytes_per_launch=kv_bytes_per_launch, achieved=achieved,
                reps_total=reps_total, graph=use_graph)
     return insts, fig
@@ -600,6 +602,9 @@ def main():
         },
         "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": fig["bytes_per_pass"],
+        # every byte the pass reads or writes once (queries, drafts, outputs, tables,
+        # indices, scores, split partials besides the algorithmic bytes): secondary
+        "all_bytes_per_step": fig["all_bytes_per_pass"],
         "roofline": {
             "kernel": "sv_sparse_verify_attn (attn_kernel; split partials merged inside the "
                       "launch)",

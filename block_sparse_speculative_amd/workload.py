@@ -179,3 +179,29 @@ def algorithmic_bytes(w: synth.Workload, ctx_lens, num_layers: int) -> int:
             scored_blocks += nb
     reps = scored_blocks * w.num_kv_heads * w.head_dim * 4
     return kv + reps * _select_layers(w, num_layers)
+
+
+def all_bytes(w: synth.Workload, ctx_lens, num_layers: int, k_max: int, splits: int) -> int:
+    """Every byte one pass reads or writes, counted once each (host arithmetic): the
+    algorithmic bytes, plus per layer the queries, draft K/V, outputs and block table
+    read by the attention, the indices and counts (written on selecting layers, read on
+    every layer), and with more than one split the fp32 partials (O, max, denominator)
+    written and read back once; selecting layers add the first-draft queries and table
+    read by the scoring and the block scores written and read once."""
+    esz = 4 if w.dtype == "fp32" else 2
+    B, T, Hq, Hkv, D = w.num_seqs, w.num_draft, w.num_q_heads, w.num_kv_heads, w.head_dim
+    nb_max = max(max(-(-c // w.block_size) for c in ctx_lens), 1)
+    units = B * Hkv
+    rows = T * (Hq // Hkv)
+    per_layer = (2 * B * T * Hq * D * esz          # queries in, outputs out
+                 + 2 * B * T * Hkv * D * esz       # draft K and V
+                 + B * nb_max * 4                  # block table
+                 + units * (k_max + 1) * 4)        # indices and counts read
+    if splits > 1:
+        per_layer += 2 * (splits + 1) * units * rows * (D + 2) * 4
+    per_select = (units * (k_max + 1) * 4          # indices and counts written
+                  + B * Hq * D * esz               # first-draft queries for the scores
+                  + B * nb_max * 4                 # block table for the scores
+                  + 2 * units * nb_max * 4)        # scores written and read
+    return (algorithmic_bytes(w, ctx_lens, num_layers) + num_layers * per_layer
+            + _select_layers(w, num_layers) * per_select)

@@ -55,3 +55,17 @@ def test_counter_fields_follow_the_kernel_source(tmp_path, monkeypatch):
     assert bench.counter_field("other", "traffic_bytes_per_launch") is None
     src.write_text("changed kernel source\n")   # counters now belong to another source
     assert bench.counter_field("w", "traffic_bytes_per_launch") is None
+
+
+def test_all_bytes_counts_each_buffer_once():
+    # the c0 shape (1 seq, 8/2 heads, d 64, fp32, bs 32, T 4, ctx 2048, k 16), by hand:
+    # algorithmic 557056 (512 tokens x 2 heads x 64 x K,V x 4 B + 64 x 2 x 64 x 4 B reps);
+    # per layer: Q in + O out 16384, draft K/V 4096, table 256, indices read 136;
+    # selecting layer: indices written 136, first-draft Q 2048, table 256, scores 1024;
+    # split partials (S + 1) x 2 units x 16 rows x 66 floats x 4 B, written and read
+    from block_sparse_speculative_amd import synth
+    from block_sparse_speculative_amd import workload as WL
+    w = synth.WORKLOADS["tiny"]
+    assert WL.algorithmic_bytes(w, [2048], 1) == 557056
+    assert WL.all_bytes(w, [2048], 1, 16, 1) == 557056 + 16384 + 4096 + 256 + 136 + 3464
+    assert WL.all_bytes(w, [2048], 1, 16, 3) == 581392 + 2 * 4 * 2 * 16 * 66 * 4
