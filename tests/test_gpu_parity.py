@@ -531,6 +531,39 @@ def test_merge_with_other_kernels_holding_the_device():
     run_and_check(inst, units=[(0, 0), (1, 3), (2, 5), (3, 7)], case="merge under load")
 
 
+def test_independent_passes_on_concurrent_streams():
+    # Two instances with their own buffers and workspaces run their passes at the same
+    # time on two streams (same priority): the library keeps no state between calls
+    # beyond the caller's buffers, so each result is bit-identical to its pass run alone.
+    _gpu()
+    a = Instance(W["stack64k"].with_(num_layers=2, ctx=(8192,) * 4), seed=41, fused=True)
+    b = Instance(SMALL["ragged_small"].with_(num_layers=2, reuse_odd_layers=True), seed=42)
+    alone = []
+    for x in (a, b):
+        x.step()
+        torch.cuda.synchronize()
+        alone.append([(ly.out.clone(), ly.lse.clone(), ly.idx.clone(), ly.cnt.clone())
+                      for ly in x.layers])
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        for x in (a, b):
+            for ly in x.layers:
+                ly.out.fill_(float("nan"))
+                ly.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sa):
+            a.step()
+        with torch.cuda.stream(sb):
+            b.step()
+        torch.cuda.synchronize()
+        for x, ref in zip((a, b), alone):
+            for ly, (o, l_, i_, c_) in zip(x.layers, ref):
+                assert torch.equal(ly.out, o) and torch.equal(ly.lse, l_), f"replay {rep}"
+                assert torch.equal(ly.idx, i_) and torch.equal(ly.cnt, c_), f"replay {rep}"
+    run_and_check(a, units=[(0, 0), (3, 7)], case="concurrent streams, stack64k shape")
+    run_and_check(b, case="concurrent streams, ragged")
+
+
 def test_workspace_grown_to_more_units_after_zero_fill():
     # A workspace used by calls of 2 units and then (after the documented zero-fill) of
     # 4 units, with a one-split call in between, gives exactly what fresh workspaces give.
