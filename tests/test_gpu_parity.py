@@ -531,6 +531,26 @@ def test_merge_with_other_kernels_holding_the_device():
     run_and_check(inst, units=[(0, 0), (1, 3), (2, 5), (3, 7)], case="merge under load")
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("splits", [0, 1])
+def test_largest_block_table_and_row_count(fused, splits):
+    # The envelope's limits together: 16384 blocks per sequence (512K tokens in 32-token
+    # blocks: the LDS radix top-k, the unstaged table, and with the library's split count
+    # the merge kernel) and 128 rows per unit (16 drafts x a GQA group of 8).
+    _gpu()
+    w = W["llama32k"].with_(num_seqs=1, num_q_heads=8, num_kv_heads=1, head_dim=64,
+                            block_size=32, num_draft=16, ctx=(16384 * 32,),
+                            budget=(0, 64, 30, 1, 1))
+    PT.log(f"[largest] fused={fused} splits={splits}")
+    inst = Instance(w, seed=51, num_splits=splits, fused=fused, nan_pool=True)
+    assert inst.shape.max_blocks_per_seq == 16384 and inst.k_max == 492
+    PT.log(f"  plan {inst.plan}")
+    run_and_check(inst, case=f"16384 blocks, 128 rows, {'fused' if fused else 'separate'} "
+                             f"s{splits}")
+    del inst
+    _free()
+
+
 def test_independent_passes_on_concurrent_streams():
     # Two instances with their own buffers and workspaces run their passes at the same
     # time on two streams (same priority): the library keeps no state between calls
