@@ -6,7 +6,9 @@
  *                            append with representatives (sv_block_repr), selection
  *                            (sv_select_blocks), attention on the selection
  *                            (sv_sparse_verify_attn), the fused call
- *                            (sv_select_and_attend), reuse (sv_reuse_indices) and a
+ *                            (sv_select_and_attend) and its allocation-free form
+ *                            (sv_select_and_attend_static, whose results must equal the
+ *                            fused call's bit for bit), reuse (sv_reuse_indices) and a
  *                            threshold-pruned FFN (sv_sparse_ffn). Inputs and outputs
  *                            are written to OUTDIR as raw little-endian arrays, with
  *                            their sizes in OUTDIR/meta.txt, for a check against the
@@ -190,6 +192,18 @@ static int download_save(const char* dir, const char* name, const void* dev, siz
   return rc;
 }
 
+/* 1 when two device arrays hold the same bytes */
+static int same_on_device(const void* a, const void* b, size_t bytes) {
+  unsigned char* ha = malloc(bytes);
+  unsigned char* hb = malloc(bytes);
+  int same = ha && hb && hipMemcpy(ha, a, bytes, hipMemcpyDeviceToHost) == hipSuccess &&
+             hipMemcpy(hb, b, bytes, hipMemcpyDeviceToHost) == hipSuccess &&
+             memcmp(ha, hb, bytes) == 0;
+  free(ha);
+  free(hb);
+  return same;
+}
+
 enum { B = 2, HQ = 8, HKV = 2, D = 128, BS = 64, T = 4, KMAX = 8 };
 static const int32_t CTX[B] = {1000, 2500};
 
@@ -215,7 +229,7 @@ static int gpu_run(const char* dir) {
   void *d_knew, *d_vnew, *d_q, *d_kd, *d_vd, *d_kpool, *d_vpool, *d_reps, *d_table, *d_ctx,
       *d_nnew, *d_cbefore, *d_cafter, *d_idx, *d_cnt, *d_scores, *d_out, *d_lse, *d_idx2,
       *d_cnt2, *d_out2, *d_lse2, *d_idx3, *d_cnt3, *d_wsel, *d_wattn, *d_wfused, *d_x, *d_wg,
-      *d_wu, *d_wd, *d_y, *d_keep, *d_wffn;
+      *d_wu, *d_wd, *d_y, *d_keep, *d_wffn, *d_idx4, *d_cnt4, *d_out4, *d_lse4;
   size_t n_wsel, n_wattn, n_wfused, n_wffn;
   int32_t i, j;
   FILE* meta;
@@ -280,7 +294,9 @@ static int gpu_run(const char* dir) {
       upload(&d_wfused, NULL, n_wfused) || upload(&d_x, x, n_x * 2) ||
       upload(&d_wg, wg, n_w * 2) || upload(&d_wu, wu, n_w * 2) || upload(&d_wd, wd, n_w * 2) ||
       upload(&d_y, NULL, n_x * 2) || upload(&d_keep, NULL, (size_t)fs.d_ffn * 4) ||
-      upload(&d_wffn, NULL, n_wffn)) {
+      upload(&d_wffn, NULL, n_wffn) || upload(&d_idx4, NULL, n_idx * 4) ||
+      upload(&d_cnt4, NULL, n_cnt * 4) || upload(&d_out4, NULL, n_q * 2) ||
+      upload(&d_lse4, NULL, n_lse * 4)) {
     fprintf(stderr, "device allocation or copy failed\n");
     return 1;
   }
@@ -296,9 +312,14 @@ static int gpu_run(const char* dir) {
   CHECK_SV(sv_select_and_attend(&s, &budget, d_q, d_reps, d_kd, d_vd, NULL, d_kpool, d_vpool,
                                 d_table, d_ctx, KMAX, scale, 0, d_idx2, d_cnt2, d_out2, d_lse2,
                                 d_wfused, n_wfused, NULL));
+  CHECK_SV(sv_select_and_attend_static(&s, &budget, d_q, d_reps, d_kd, d_vd, NULL, d_kpool,
+                                       d_vpool, d_table, d_ctx, KMAX, scale, 0, d_idx4, d_cnt4,
+                                       d_out4, d_lse4, NULL));
   CHECK_SV(sv_reuse_indices(&s, KMAX, d_idx, d_cnt, d_idx3, d_cnt3, NULL));
   CHECK_SV(sv_sparse_ffn(&fs, d_x, d_wg, d_wu, d_wd, tau, d_y, d_keep, d_wffn, n_wffn, NULL));
   CHECK_HIP(hipDeviceSynchronize());
+  EXPECT(same_on_device(d_idx4, d_idx2, n_idx * 4) && same_on_device(d_cnt4, d_cnt2, n_cnt * 4));
+  EXPECT(same_on_device(d_out4, d_out2, n_q * 2) && same_on_device(d_lse4, d_lse2, n_lse * 4));
 
   snprintf(path, sizeof path, "%s/meta.txt", dir);
   meta = fopen(path, "w");

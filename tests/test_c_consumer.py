@@ -15,6 +15,7 @@ against the oracle:
   - the selection matches (exact, or the near-tie rule);
   - attention on the selection and the fused call both match within the bf16 bound;
   - the fused call selects exactly what the separate call does;
+  - the allocation-free fused call equals the fused call bit for bit (compared in C);
   - reuse copies exactly;
   - the FFN keeps and output match within the bound derived for it.
 """
